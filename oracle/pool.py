@@ -1,0 +1,67 @@
+"""The paged K/V pool as the kernels see it (oracle).
+
+Source: transcript paragraph 3 (equal blocks anywhere in a shared pool, a
+table per request) and "Inside vLLM and TGI", section "Block addresses and
+fragmentation arithmetic" (block, offset addressing).
+
+The pool is `num_blocks * b` slots; slot s is offset s % b of block s // b.
+Each slot holds an opaque payload reference or None (never written: its
+device bytes are whatever the pool was filled with).  Two operations change
+it, mirroring the device side effects of the allocator:
+  write(slot, payload)   one token's K and V rows for every KV head
+  copy(src, dst)         every slot of block src into block dst (all b slots,
+                         written or not)
+Values are resolved only when asked, in fp64, in the layout
+[block][offset][kv head][dim] -- deliberately not the device layout.
+"""
+from __future__ import annotations
+
+from typing import Any, Callable, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+class SlotPool:
+    def __init__(self, num_blocks: int, width: int):
+        self.num_blocks = num_blocks
+        self.width = width
+        self.slots: List[Optional[Any]] = [None] * (num_blocks * width)
+
+    def write(self, slot: int, payload: Any) -> None:
+        if slot < 0:
+            return                                  # negative slot: nothing written
+        self.slots[slot] = payload
+
+    def copy(self, src: int, dst: int) -> None:
+        b = self.width
+        self.slots[dst * b:(dst + 1) * b] = self.slots[src * b:(src + 1) * b]
+
+    def replay(self, events: Iterable[Tuple[str, int, Any]]) -> None:
+        for kind, a, c in events:
+            if kind == "write":
+                self.write(a, c)
+            elif kind == "copy":
+                self.copy(a, c)
+            else:
+                raise ValueError(kind)
+
+    def block_payloads(self, blk: int) -> List[Optional[Any]]:
+        b = self.width
+        return self.slots[blk * b:(blk + 1) * b]
+
+    def materialize(self, resolve: Callable[[Any], Tuple[np.ndarray, np.ndarray]],
+                    num_kv_heads: int, head_dim: int,
+                    blocks: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """fp64 K, V of the listed blocks (all by default) as [n][b][Hkv][d]; NaN where unwritten."""
+        blocks = range(self.num_blocks) if blocks is None else blocks
+        blocks = list(blocks)
+        shape = (len(blocks), self.width, num_kv_heads, head_dim)
+        K = np.full(shape, np.nan)
+        V = np.full(shape, np.nan)
+        for i, blk in enumerate(blocks):
+            for o, p in enumerate(self.block_payloads(blk)):
+                if p is not None:
+                    k, v = resolve(p)
+                    K[i, o] = k
+                    V[i, o] = v
+        return K, V
