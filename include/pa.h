@@ -1,0 +1,216 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV cache and single-query decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages this project follows):
+ *   - A pool of equal-size blocks holds the K and V vectors of many requests;
+ *     each request has a block table mapping its logical blocks to physical
+ *     blocks anywhere in the pool; position t of a request lives at offset
+ *     t % b of physical block table[t / b].  ("Inside vLLM and TGI: Paging,
+ *     Versioned Schedulers and Operations", section "Block addresses and
+ *     fragmentation arithmetic"; "vLLM and PagedAttention: Virtual Memory for
+ *     LLM Serving", paragraph 3.)
+ *   - Decode attention reads a request's K/V through its table: for query
+ *     head h of sequence i, with G = Hq / Hkv and g = h / G,
+ *       s_t = scale * <q[i][h], K_i[t][g]>,  w = softmax(s over t < L_i),
+ *       out[i][h] = sum_t w_t V_i[t][g].
+ *     (transcript paragraph 3: the attention kernel reads through the
+ *     mapping; the pages do not write the formula -- this is ordinary scaled
+ *     dot-product attention of one query.)
+ *   - Growing a request writes its new token's K/V into the slot its table
+ *     gives; a shared, partially filled last block is copied to a private
+ *     block before a write (copy-on-write).  ("Inside vLLM and TGI", section
+ *     "Exact CPU block manager and copy-on-write"; transcript paragraph 4.)
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer.  The library allocates and
+ *     frees nothing and keeps no state between calls (no handles; calls are
+ *     thread-safe).  Pointers marked "device" are device memory of the
+ *     current HIP device; pointers marked "host" are host memory.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Every call that takes a stream only enqueues work on it and
+ *     returns; inputs must stay alive and unmodified until the stream has
+ *     passed the call (the stream form of "a worker still holding a lease
+ *     keeps its blocks", "Inside vLLM and TGI", section "Exact CPU block
+ *     manager and copy-on-write", last paragraphs).
+ *   - Errors: host-side argument checks run first; a failed check returns a
+ *     status and enqueues NOTHING, so a failing call has no side effect
+ *     (the pages' atomic-failure rule for admission and copy-on-write).  A
+ *     HIP launch error is reported as PA_ERR_HIP.  No exception crosses the
+ *     ABI.
+ *   - Device-resident contents (tables, lengths, slots, pairs) are not read
+ *     by the host.  Kernels never access memory outside the buffers they are
+ *     given: a table entry outside [0, num_blocks) contributes no tokens, a
+ *     slot outside the pool is skipped, a length larger than the table or the
+ *     stated maximum is clipped.  Results for such inputs are unspecified;
+ *     pa_validate_tables reports them ("Before a real kernel consumes a
+ *     table, validate ownership, bounds, cache dtype and logical length",
+ *     "Inside vLLM and TGI", same section).
+ *
+ * Pool layout (the ABI of the cache; chosen for gfx950, see each kernel)
+ *   Two separate pools, K and V, each num_blocks * Hkv tiles of
+ *   block_size * head_dim elements; tile (blk, h) starts at element
+ *   (blk * Hkv + h) * block_size * head_dim, so every (block, KV head) tile is
+ *   one contiguous 4 KiB run for 16 x 128 16-bit or 16 x 64 fp32 elements.
+ *   Inside a tile, with X = 16 / sizeof(element) (8 for f16/bf16, 4 for f32):
+ *     K: element (offset o, dim d) at ((d / X) * block_size + o) * X + d % X
+ *        -- 16-byte vectors of X consecutive dims, token-major within a
+ *        vector column ("[d/X][b][X]");
+ *     V: element (offset o, dim d) at d * block_size + o
+ *        -- transposed, tokens contiguous per dim ("[d][b]").
+ *   Both make the decode kernel's per-instruction loads one contiguous run.
+ *
+ * Supported shapes: block_size 16; head_dim 64 or 128; dtype f32, f16, bf16;
+ * 1 <= num_q_heads / num_kv_heads <= 16 and num_q_heads % num_kv_heads == 0.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported with default visibility. */
+#define PA_API __attribute__((visibility("default")))
+
+typedef int32_t pa_status;
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent shape */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not built: dtype, head_dim, block_size, group */
+  PA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than pa_decode_workspace_size */
+  PA_ERR_HIP = 4           /* the HIP runtime reported an error for a launch */
+};
+
+typedef int32_t pa_dtype;
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+
+/* Describes a K/V pool pair (layout above).  Passed by pointer, read only
+ * during the call. */
+typedef struct pa_pool_desc {
+  int32_t num_blocks;    /* physical blocks in each pool, >= 1 */
+  int32_t block_size;    /* tokens per block (b); 16 */
+  int32_t num_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;      /* 64 or 128 */
+  pa_dtype dtype;        /* element type of both pools */
+} pa_pool_desc;
+
+/* Human-readable name of a status; never NULL, static storage. */
+PA_API const char* pa_status_string(pa_status s);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+PA_API int32_t pa_version(void);
+
+/*
+ * pa_slot_mapping -- address translation for new tokens.
+ *   slots[t] = table[seq][p / b] * b + p % b, with seq = seq_ids[t], p = positions[t]
+ * ("Inside vLLM and TGI", section "Block addresses and fragmentation
+ * arithmetic": logical block t // b, offset t % b, physical table[t // b]).
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq], row-major
+ *   seq_ids       device int32 [n]: row of block_tables for token t
+ *   positions     device int32 [n]: zero-based position of token t
+ *   slots         device int32 [n] (output); -1 where seq_id is outside
+ *                 [0, num_seqs), the position is negative or past the table
+ *                 row, the table entry is negative, or the slot overflows int32
+ * n == 0 enqueues nothing and returns PA_OK.
+ */
+PA_API pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, const int32_t* seq_ids, const int32_t* positions,
+                          int32_t n, int32_t block_size, int32_t* slots, void* stream);
+
+/*
+ * pa_write_kv -- write new tokens' K and V into their pool slots
+ * (the device side of growing a request: "Inside vLLM and TGI", section
+ * "Exact CPU block manager and copy-on-write"; transcript paragraph 3).
+ *   k_pool, v_pool   device, pool layout above (written)
+ *   k_new, v_new     device, pool dtype; token t, KV head h, dim d at
+ *                    element t * new_stride + h * head_dim + d
+ *   new_stride       elements between consecutive tokens (>= Hkv * head_dim;
+ *                    Hkv * head_dim when contiguous [n][Hkv][d])
+ *   slot_mapping     device int32 [n]; slot s is offset s % b of block s / b;
+ *                    a slot < 0 or >= num_blocks * b is skipped
+ * Bytes are copied unchanged (no conversion).  Two tokens with the same slot
+ * in one call: unspecified which one lands.
+ */
+PA_API pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, int64_t new_stride, const int32_t* slot_mapping,
+                      int32_t n, void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole blocks, all KV heads, in both pools
+ * (copy-on-write of a shared partial last block: "Inside vLLM and TGI",
+ * section "Exact CPU block manager and copy-on-write"; transcript paragraph 4).
+ *   block_pairs  device int32 [n_pairs][2] = {src, dst}; a pair with an id
+ *                outside [0, num_blocks) is skipped
+ * Every dst must be distinct and must not appear as any src in the same call
+ * (otherwise the result is unspecified).  n_pairs == 0 enqueues nothing.
+ */
+PA_API pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                         const int32_t* block_pairs, int32_t n_pairs, void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode_attention
+ * needs for these arguments (0 when partition_size == 0 or when every
+ * sequence fits in one partition).  `bytes` is host memory.
+ */
+PA_API pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_context_len,
+                                   int32_t partition_size, size_t* bytes);
+
+/*
+ * pa_decode_attention -- single-query decode attention through block tables
+ * (formula at the top of this file).
+ *   k_pool, v_pool    device, pool layout above (read)
+ *   q                 device [num_seqs][num_q_heads][head_dim], pool dtype
+ *   out               device [num_seqs][num_q_heads][head_dim] of out_dtype
+ *                     (PA_F32, or the pool dtype: rounded to nearest even);
+ *                     must not alias q or the pools
+ *   block_tables      device int32 [num_seqs][max_blocks_per_seq]; entries
+ *                     past ceil(L_i / b) are never read
+ *   context_lens      device int32 [num_seqs]: L_i = number of stored tokens
+ *                     attended to (positions 0 .. L_i - 1); L_i == 0 gives a
+ *                     zero output row
+ *   scale             multiplier of q.k (e.g. 1/sqrt(head_dim))
+ *   max_context_len   host upper bound of every L_i (sizes the grid); lengths
+ *                     above it are clipped to it
+ *   partition_size    0: each (sequence, KV head) is one work unit; else
+ *                     positions are split into consecutive partitions of
+ *                     partition_size tokens (a positive multiple of
+ *                     block_size), processed independently and combined by
+ *                     a second kernel that rescales each partition's
+ *                     (max, sum, weighted sum) to the global max
+ *   workspace         device, >= pa_decode_workspace_size bytes (may be NULL
+ *                     when that size is 0)
+ * Accumulation is fp32 in every dtype; q.k products of f16/bf16 inputs are
+ * exact in fp32.
+ */
+PA_API pa_status pa_decode_attention(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
+                              const void* q, void* out, pa_dtype out_dtype,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, float scale, int32_t max_context_len,
+                              int32_t partition_size, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * pa_validate_tables -- debug check of device-resident tables before a
+ * kernel consumes them ("Inside vLLM and TGI", section "Exact CPU block
+ * manager and copy-on-write", validation paragraph).  Counts violations:
+ * a length outside [1, min(max_context_len, max_blocks_per_seq * b)], or a
+ * table entry j < ceil(L_i / b) outside [0, num_blocks).
+ *   bad_count   device int32 [1] (output): number of violations
+ * Asynchronous like every other call; read bad_count after the stream passes.
+ */
+PA_API pa_status pa_validate_tables(const pa_pool_desc* pool, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t max_context_len, int32_t* bad_count,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

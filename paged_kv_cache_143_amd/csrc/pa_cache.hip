@@ -1,0 +1,229 @@
+// Cache-side kernels of libpa: slot mapping, token writes, block copies and
+// table validation.  All are byte movers or integer arithmetic; the bound is
+// HBM bandwidth (or launch latency at decode sizes).
+//
+// Address rule ("Inside vLLM and TGI: Paging, Versioned Schedulers and
+// Operations", section "Block addresses and fragmentation arithmetic"):
+// position t lives at offset t % b of physical block table[t / b].
+// Copy-on-write of a shared partial last block (same page, section "Exact
+// CPU block manager and copy-on-write"; "vLLM and PagedAttention"
+// transcript, paragraph 4) is a whole-block copy in both pools.
+#include "pa_internal.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// slot = table[seq][p / b] * b + p % b   (one thread per new token)
+// ---------------------------------------------------------------------------
+__global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t max_blocks,
+                                    int32_t num_seqs, const int32_t* __restrict__ seq_ids,
+                                    const int32_t* __restrict__ positions, int32_t n,
+                                    int32_t block_size, int32_t* __restrict__ slots) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const int32_t s = seq_ids[t];
+  const int32_t pos = positions[t];
+  int32_t out = -1;
+  if (s >= 0 && s < num_seqs && pos >= 0) {
+    const int32_t j = pos / block_size;
+    if (j < max_blocks) {
+      const int32_t phys = tables[(int64_t)s * max_blocks + j];
+      const int64_t flat = (int64_t)phys * block_size + pos % block_size;
+      if (phys >= 0 && flat <= INT32_MAX) out = (int32_t)flat;
+    }
+  }
+  slots[t] = out;
+}
+
+// ---------------------------------------------------------------------------
+// Token writes.  One thread moves one 16-byte vector of X consecutive dims of
+// one (token, KV head).  K goes to the [d/X][b][X] tile as one 16-byte store;
+// V goes to the transposed [d][b] tile as X element stores (stride b).
+// ---------------------------------------------------------------------------
+template <int ES>  // element size in bytes: 2 or 4
+__global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                const char* __restrict__ k_new, const char* __restrict__ v_new,
+                                int64_t new_stride, const int32_t* __restrict__ slots, int32_t n,
+                                int32_t num_heads, int32_t head_dim, int64_t num_slots) {
+  constexpr int X = 16 / ES;
+  const int chunks = head_dim / X;                 // vectors per (token, head)
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tok = (int64_t)num_heads * chunks;
+  if (gid >= (int64_t)n * per_tok) return;
+  const int t = (int)(gid / per_tok);
+  const int rem = (int)(gid - (int64_t)t * per_tok);
+  const int h = rem / chunks;
+  const int c = rem - h * chunks;
+  const int32_t slot = slots[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int32_t blk = slot / kBlock;
+  const int32_t off = slot - blk * kBlock;
+  const int64_t src = ((int64_t)t * new_stride + (int64_t)h * head_dim + (int64_t)c * X) * ES;
+  const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)kBlock * head_dim;   // elements
+  // K: vector column c, row `off`.
+  const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + src);
+  *reinterpret_cast<u32x4*>(k_pool + (tile + ((int64_t)c * kBlock + off) * X) * ES) = kv;
+  // V: dims c*X .. c*X+X-1 of token `off`, transposed.
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + src);
+  char* vt = v_pool + (tile + (int64_t)c * X * kBlock + off) * ES;
+  if constexpr (ES == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vt + (int64_t)e * kBlock * 4) = vv[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t half = (uint16_t)(vv[e >> 1] >> ((e & 1) * 16));
+      *reinterpret_cast<uint16_t*>(vt + (int64_t)e * kBlock * 2) = half;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole-block copies: every 16-byte vector of the (src) block in both pools.
+// ---------------------------------------------------------------------------
+__global__ void copy_blocks_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                   const int32_t* __restrict__ pairs, int32_t n_pairs,
+                                   int64_t block_vecs, int32_t num_blocks) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_pair = 2 * block_vecs;
+  if (gid >= (int64_t)n_pairs * per_pair) return;
+  const int p = (int)(gid / per_pair);
+  int64_t r = gid - (int64_t)p * per_pair;
+  char* pool = k_pool;
+  if (r >= block_vecs) { pool = v_pool; r -= block_vecs; }
+  const int32_t src = pairs[2 * p];
+  const int32_t dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const u32x4* s = reinterpret_cast<const u32x4*>(pool) + (int64_t)src * block_vecs + r;
+  u32x4* d = reinterpret_cast<u32x4*>(pool) + (int64_t)dst * block_vecs + r;
+  *d = *s;
+}
+
+// ---------------------------------------------------------------------------
+// Validation: count lengths out of range and referenced entries out of range.
+// ---------------------------------------------------------------------------
+__global__ void zero_int_kernel(int32_t* p) { *p = 0; }
+
+__global__ void validate_kernel(const int32_t* __restrict__ tables, int32_t max_blocks,
+                                const int32_t* __restrict__ lens, int32_t num_seqs,
+                                int32_t max_len, int32_t num_blocks, int32_t* bad) {
+  const int s = blockIdx.x;
+  if (s >= num_seqs) return;
+  const int32_t L = lens[s];
+  const int64_t cap = (int64_t)max_blocks * kBlock;
+  int32_t local = 0;
+  int32_t check_blocks;
+  if (L < 1 || L > max_len || (int64_t)L > cap) {
+    if (threadIdx.x == 0) local += 1;
+    check_blocks = (L < 1) ? 0 : (int32_t)min<int64_t>((L + kBlock - 1) / kBlock, max_blocks);
+  } else {
+    check_blocks = (L + kBlock - 1) / kBlock;
+  }
+  for (int j = threadIdx.x; j < check_blocks; j += blockDim.x) {
+    const int32_t phys = tables[(int64_t)s * max_blocks + j];
+    if (phys < 0 || phys >= num_blocks) local += 1;
+  }
+  if (local) atomicAdd(bad, local);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t pa_version(void) { return 100; }
+
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, const int32_t* seq_ids, const int32_t* positions,
+                          int32_t n, int32_t block_size, int32_t* slots, void* stream) {
+  if (n < 0 || num_seqs < 0 || max_blocks_per_seq < 0 || block_size < 1) return PA_ERR_INVALID_ARG;
+  if (n == 0) return PA_OK;
+  if (!seq_ids || !positions || !slots) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
+  const int threads = 256;
+  slot_mapping_kernel<<<(n + threads - 1) / threads, threads, 0, (hipStream_t)stream>>>(
+      block_tables, max_blocks_per_seq, num_seqs, seq_ids, positions, n, block_size, slots);
+  return launch_status();
+}
+
+pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, int64_t new_stride, const int32_t* slot_mapping,
+                      int32_t n, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_INVALID_ARG;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  const int es = elem_bytes(pool->dtype);
+  const int64_t row = (int64_t)pool->num_kv_heads * pool->head_dim;
+  if (new_stride < row) return PA_ERR_INVALID_ARG;
+  // 16-byte vector moves need 16-byte aligned pools, rows and token strides.
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
+      (new_stride * es) % 16 != 0)
+    return PA_ERR_INVALID_ARG;
+  const int64_t vecs = (int64_t)n * pool->num_kv_heads * (pool->head_dim * es / 16);
+  const int threads = 256;
+  const int64_t blocks = (vecs + threads - 1) / threads;
+  if (blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const int64_t num_slots = (int64_t)pool->num_blocks * pool->block_size;
+  if (es == 2)
+    write_kv_kernel<2><<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
+        (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
+        slot_mapping, n, pool->num_kv_heads, pool->head_dim, num_slots);
+  else
+    write_kv_kernel<4><<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
+        (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
+        slot_mapping, n, pool->num_kv_heads, pool->head_dim, num_slots);
+  return launch_status();
+}
+
+pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                         const int32_t* block_pairs, int32_t n_pairs, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (n_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (n_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_pairs) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes = (int64_t)pool->num_kv_heads * tile_elems(pool) * elem_bytes(pool->dtype);
+  const int64_t block_vecs = block_bytes / 16;
+  const int64_t total = (int64_t)n_pairs * 2 * block_vecs;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  copy_blocks_kernel<<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
+      (char*)k_pool, (char*)v_pool, block_pairs, n_pairs, block_vecs, pool->num_blocks);
+  return launch_status();
+}
+
+pa_status pa_validate_tables(const pa_pool_desc* pool, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t max_context_len, int32_t* bad_count,
+                             void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0 || !bad_count)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables)))
+    return PA_ERR_INVALID_ARG;
+  zero_int_kernel<<<1, 1, 0, (hipStream_t)stream>>>(bad_count);
+  if (num_seqs > 0)
+    validate_kernel<<<num_seqs, 256, 0, (hipStream_t)stream>>>(
+        block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+        pool->num_blocks, bad_count);
+  return launch_status();
+}
+
+}  // extern "C"

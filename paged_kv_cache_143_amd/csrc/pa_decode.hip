@@ -1,0 +1,569 @@
+// Single-query paged decode attention for gfx950 (MI355X).
+//
+// What it computes: for sequence i, query head h (KV head g = h / G) and the
+// L_i tokens stored through block table i,
+//     out[i][h] = sum_t softmax_t(scale * q[i][h] . K_i[t][g]) V_i[t][g],
+// with K_i[t] read at offset t % 16 of physical block table_i[t / 16]
+// ("vLLM and PagedAttention: Virtual Memory for LLM Serving", paragraph 3:
+// the kernel reads through the block table and token order stays correct;
+// "Inside vLLM and TGI: Paging, Versioned Schedulers and Operations",
+// section "Block addresses and fragmentation arithmetic").  The pages give
+// neither the formula nor a kernel; this is ordinary scaled dot-product
+// attention, computed with a running (online) softmax.
+//
+// Work decomposition.  A workgroup of 4 wavefronts owns one work unit:
+// (KV head g, sequence i, partition p) where a partition is `ps`
+// consecutive positions (the whole sequence when ps covers it).  Wavefront w
+// takes the unit's blocks j = j0 + w, j0 + w + 4, ...  Per block it
+//   1. reads the physical id from the table (a register loaded once for up to
+//      64 blocks, broadcast with readlane),
+//   2. loads the K tile (4 KiB: 4 x 1 KiB fully contiguous dwordx4 loads per
+//      wavefront, for 16 x 128 16-bit elements) and the V tile (8 x 512 B
+//      contiguous dwordx2 loads), one block ahead of the computation,
+//   3. S[t][h] = K[t] . q[h] on the matrix cores: v_mfma_f32_16x16x32 with the
+//      16 tokens of the block as rows and the G <= 16 query heads of the group
+//      as columns (rows of q beyond G are zero), accumulated over head_dim,
+//   4. online softmax on the 16 x G scores (wavefront max across the four
+//      16-lane rows), in the log2 domain,
+//   5. acc[d][h] += V^T[d][t] P[t][h], again v_mfma_f32_16x16x32, whose B
+//      operand is exactly the register layout S came out in: P is split into
+//      a high and a low 16-bit part (P = hi + lo to about 2^-17), placed in the
+//      two halves of the k dimension against a duplicated V fragment, so the
+//      products keep fp32-level accuracy.
+// The four wavefronts' (m, l, acc) are merged in LDS; a single-partition unit
+// writes the normalised output, otherwise (m, l, o / l) partials go to the
+// workspace and a reduce kernel rescales them by exp2(m_p - max m).
+//
+// fp32 pools use v_mfma_f32_16x16x4_f32 in the same roles (one k per lane).
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct TagF32 {};
+struct TagF16 {};
+struct TagBF16 {};
+
+template <class Tag> struct Is16 { static constexpr bool value = true; };
+template <> struct Is16<TagF32> { static constexpr bool value = false; };
+
+struct DecodeArgs {
+  const char* k_pool;
+  const char* v_pool;
+  const char* q;
+  void* out;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* part_m;       // [S][Hq][P]
+  float* part_l;       // [S][Hq][P]
+  float* part_o;       // [S][Hq][P][D]
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t group;       // G = Hq / Hkv
+  int32_t num_seqs;
+  int32_t max_blocks;  // table row width
+  int32_t max_len;     // clip for lengths
+  int32_t ps;          // partition size in tokens (multiple of 16)
+  int32_t num_parts;   // P = ceil(max_len / ps)
+  float qk_scale;      // scale * log2(e)
+};
+
+// ---- matrix-core wrappers -------------------------------------------------
+template <class Tag> __device__ inline f32x4 mma32(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ inline f32x4 mma32<TagBF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ inline f32x4 mma32<TagF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even narrowing of p to 16 bits, and the residual.
+template <class Tag> __device__ inline uint32_t narrow16(float x);
+template <> __device__ inline uint32_t narrow16<TagBF16>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+template <> __device__ inline uint32_t narrow16<TagF16>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+template <class Tag> __device__ inline float widen16(uint32_t bits);
+template <> __device__ inline float widen16<TagBF16>(uint32_t bits) {
+  return __builtin_bit_cast(float, bits << 16);
+}
+template <> __device__ inline float widen16<TagF16>(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ inline float xor_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---- per-block register fragments ------------------------------------------
+// 16-bit: K tile [d/8][16][8] -> load m gives lane (t = lane%16) the 8 dims
+// 8*(4m + lane/16) ..; V tile [d][16] -> load n gives lane (d = 16n + lane%16)
+// the 4 tokens 4*(lane/16) ...
+template <class Tag, int D, bool H = Is16<Tag>::value> struct Frag;
+
+template <class Tag, int D> struct Frag<Tag, D, true> {
+  static constexpr int NK = D / 32;
+  static constexpr int NV = D / 16;
+  u32x4 k[NK];
+  u32x2 v[NV];
+  __device__ inline void load(const char* kt, const char* vt, int lane) {
+#pragma unroll
+    for (int m = 0; m < NK; ++m)
+      k[m] = *reinterpret_cast<const u32x4*>(kt + m * 1024 + lane * 16);
+    const int off = (lane & 15) * 32 + (lane >> 4) * 8;
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+      v[n] = *reinterpret_cast<const u32x2*>(vt + n * 512 + off);
+  }
+};
+
+// fp32: K tile [d/4][16][4] -> load j gives lane (t = lane%16) dims
+// 4*(4j + lane/16) ..; V tile [d][16] -> load n gives lane (d = 16n + lane%16)
+// the 4 tokens 4*(lane/16) ...
+template <class Tag, int D> struct Frag<Tag, D, false> {
+  static constexpr int NK = D / 16;
+  static constexpr int NV = D / 16;
+  f32x4 k[NK];
+  f32x4 v[NV];
+  __device__ inline void load(const char* kt, const char* vt, int lane) {
+#pragma unroll
+    for (int j = 0; j < NK; ++j)
+      k[j] = *reinterpret_cast<const f32x4*>(kt + j * 1024 + lane * 16);
+    const int off = (lane & 15) * 64 + (lane >> 4) * 16;
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+      v[n] = *reinterpret_cast<const f32x4*>(vt + n * 1024 + off);
+  }
+};
+
+// Query fragment: the B operand of S = K q^T for head (lane % 16) of the group.
+template <class Tag, int D, bool H = Is16<Tag>::value> struct QFrag;
+template <class Tag, int D> struct QFrag<Tag, D, true> {
+  u32x4 q[D / 32];
+  __device__ inline void load(const char* qrow, bool valid, int lane) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const int dim0 = 8 * (4 * m + (lane >> 4));
+      q[m] = valid ? *reinterpret_cast<const u32x4*>(qrow + dim0 * 2) : u32x4{0, 0, 0, 0};
+    }
+  }
+};
+template <class Tag, int D> struct QFrag<Tag, D, false> {
+  f32x4 q[D / 16];
+  __device__ inline void load(const char* qrow, bool valid, int lane) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      const int dim0 = 4 * (4 * j + (lane >> 4));
+      q[j] = valid ? *reinterpret_cast<const f32x4*>(qrow + dim0 * 4) : f32x4{0, 0, 0, 0};
+    }
+  }
+};
+
+// Running softmax state of one wavefront: lane (h + 16 q) owns head h;
+// acc[n][r] is output dim 16n + 4q + r of that head (the MFMA C layout).
+template <int D> struct State {
+  float m;      // running max (log2 domain), identical across the head's lanes
+  float l;      // this lane's share of the running sum
+  f32x4 acc[D / 16];
+};
+
+template <class Tag, int D>
+__device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& qf, State<D>& st,
+                                    int n_valid, float qk_scale, int lane) {
+  // 1) scores S[t][h]: lane (h + 16q) gets tokens 4q..4q+3 of head h.
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (Is16<Tag>::value) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) s = mma32<Tag>(f.k[m], qf.q[m], s);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mma4(f.k[j][e], qf.q[j][e], s);
+  }
+  const int t0 = 4 * (lane >> 4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] *= qk_scale;
+    if (t0 + r >= n_valid) s[r] = -INFINITY;     // select, never multiply: tails may hold NaN
+  }
+  // 2) online softmax.
+  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  bm = xor_max(bm);
+  const float m_new = fmaxf(st.m, bm);
+  const float alpha = fast_exp2(st.m - m_new);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - m_new);
+  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  st.m = m_new;
+  // 3) acc[d][h] = alpha * acc + V^T P.
+  if constexpr (Is16<Tag>::value) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = narrow16<Tag>(p[r]);
+      lo[r] = narrow16<Tag>(p[r] - widen16<Tag>(hi[r]));
+    }
+    const u32x4 pb = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                      lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    // Tail tokens of V are zeroed (their P is zero, but 0 * NaN is NaN).
+    uint32_t keep0 = 0xffffffffu, keep1 = 0xffffffffu;
+    if (n_valid < kBlock) {
+      keep0 = (t0 + 0 < n_valid ? 0x0000ffffu : 0u) | (t0 + 1 < n_valid ? 0xffff0000u : 0u);
+      keep1 = (t0 + 2 < n_valid ? 0x0000ffffu : 0u) | (t0 + 3 < n_valid ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const uint32_t a0 = f.v[n][0] & keep0, a1 = f.v[n][1] & keep1;
+      const u32x4 va = {a0, a1, a0, a1};
+      st.acc[n] *= alpha;
+      st.acc[n] = mma32<Tag>(va, pb, st.acc[n]);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      f32x4 va = f.v[n];
+      if (n_valid < kBlock) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) va[e] = (t0 + e < n_valid) ? va[e] : 0.f;
+      }
+      st.acc[n] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.acc[n] = mma4(va[e], p[e], st.acc[n]);
+    }
+  }
+}
+
+template <class OutT> __device__ inline void store_out(OutT* o, float x);
+template <> __device__ inline void store_out<float>(float* o, float x) { *o = x; }
+template <> __device__ inline void store_out<__bf16>(__bf16* o, float x) { *o = static_cast<__bf16>(x); }
+template <> __device__ inline void store_out<_Float16>(_Float16* o, float x) { *o = static_cast<_Float16>(x); }
+
+template <class Tag> struct Elt { using T = uint16_t; static constexpr int bytes = 2; };
+template <> struct Elt<TagF32> { using T = float; static constexpr int bytes = 4; };
+
+// One workgroup per (KV head, sequence, partition); see the file comment.
+template <class Tag, int D, class OutT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  constexpr int ES = Elt<Tag>::bytes;
+  constexpr int64_t kTileBytes = (int64_t)kBlock * D * ES;
+  const int lane = threadIdx.x & (kWave - 1);
+  // The wavefront index is uniform; saying so keeps the block loop scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  const int unit = blockIdx.x;
+  const int g = unit % a.num_kv_heads;
+  const int rest = unit / a.num_kv_heads;
+  const int seq = rest % a.num_seqs;
+  const int part = rest / a.num_seqs;
+
+  int L = a.lens[seq];
+  L = L < 0 ? 0 : L;
+  L = L > a.max_len ? a.max_len : L;
+  const int64_t cap = (int64_t)a.max_blocks * kBlock;
+  if ((int64_t)L > cap) L = (int)cap;
+  const int n_parts = (L + a.ps - 1) / a.ps;
+  const int G = a.group;
+  const int head0 = g * G;
+
+  if (L == 0) {                                  // no tokens: zero output row
+    if (part == 0) {
+      OutT* o = reinterpret_cast<OutT*>(a.out) + ((int64_t)seq * a.num_q_heads + head0) * D;
+      for (int i = threadIdx.x; i < G * D; i += kThreads) store_out<OutT>(o + i, 0.f);
+    }
+    return;
+  }
+  if (part >= n_parts) return;
+
+  const int nblk_seq = (L + kBlock - 1) / kBlock;
+  const int j0 = part * (a.ps / kBlock);
+  const int j1 = min(nblk_seq, j0 + a.ps / kBlock);
+  const int first = j0 + wave;
+  const int cnt = first < j1 ? (j1 - first + kWaves - 1) / kWaves : 0;
+
+  const int h = lane & 15;
+  QFrag<Tag, D> qf;
+  qf.load(a.q + (((int64_t)seq * a.num_q_heads + head0 + (h < G ? h : 0)) * D) * ES, h < G, lane);
+
+  State<D> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
+  const int64_t head_tile = (int64_t)g * kTileBytes;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * kTileBytes;
+
+  for (int c0 = 0; c0 < cnt; c0 += kWave) {
+    const int n = min(kWave, cnt - c0);
+    const int tb = lane < n ? trow[first + kWaves * (c0 + lane)] : 0;
+    // Block i of this chunk: physical id (0 when out of range: loads stay in
+    // bounds and the block contributes nothing) and its valid-token count.
+    auto phys_of = [&](int i, int& nv) {
+      int phys = __builtin_amdgcn_readlane(tb, i);
+      const int j = first + kWaves * (c0 + i);
+      nv = min(kBlock, L - j * kBlock);
+      if (phys < 0 || phys >= a.num_blocks) { phys = 0; nv = 0; }
+      return phys;
+    };
+    // Two register buffers, one block ahead.  The steady-state loop has no
+    // conditional loads, so each computation waits only for its own block.
+    Frag<Tag, D> fa, fb;
+    int nva, nvb;
+    auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
+      const int64_t off = (int64_t)phys_of(i, nv) * block_stride + head_tile;
+      f.load(a.k_pool + off, a.v_pool + off, lane);
+    };
+    load_into(fa, 0, nva);
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+      load_into(fb, i + 1, nvb);
+      if (nva > 0) attend_block<Tag, D>(fa, qf, st, nva, a.qk_scale, lane);
+      load_into(fa, i + 2, nva);
+      if (nvb > 0) attend_block<Tag, D>(fb, qf, st, nvb, a.qk_scale, lane);
+    }
+    if (i + 1 < n) {
+      load_into(fb, i + 1, nvb);
+      if (nva > 0) attend_block<Tag, D>(fa, qf, st, nva, a.qk_scale, lane);
+      if (nvb > 0) attend_block<Tag, D>(fb, qf, st, nvb, a.qk_scale, lane);
+    } else {
+      if (nva > 0) attend_block<Tag, D>(fa, qf, st, nva, a.qk_scale, lane);
+    }
+  }
+
+  // ---- merge the four wavefronts (LDS) ----
+  const float l_tot = xor_sum(st.l);
+  float* sm_m = smem;                      // [W][G]
+  float* sm_l = smem + kWaves * G;         // [W][G]
+  float* sm_a = smem + 2 * kWaves * G;     // [W][G][D]
+  if (h < G) {
+    if (lane < 16) {
+      sm_m[wave * G + h] = st.m;
+      sm_l[wave * G + h] = l_tot;
+    }
+    float* dst = sm_a + ((int64_t)wave * G + h) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[16 * n + r] = st.acc[n][r];
+  }
+  __syncthreads();
+
+  const bool single = n_parts == 1;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int hh = idx / D;
+    const int d = idx - hh * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * G + hh]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float c = fast_exp2(sm_m[w * G + hh] - M);
+        num += c * sm_a[((int64_t)w * G + hh) * D + d];
+        den += c * sm_l[w * G + hh];
+      }
+    }
+    const float val = den > 0.f ? num / den : 0.f;
+    const int64_t row = (int64_t)seq * a.num_q_heads + head0 + hh;
+    if (single) {
+      store_out<OutT>(reinterpret_cast<OutT*>(a.out) + row * D + d, val);
+    } else {
+      a.part_o[(row * a.num_parts + part) * D + d] = val;
+      if (d == 0) {
+        a.part_m[row * a.num_parts + part] = M;
+        a.part_l[row * a.num_parts + part] = den;
+      }
+    }
+  }
+}
+
+// Combine partitions: out = sum_p c_p l_p o_p / sum_p c_p l_p, c_p = exp2(m_p - max m).
+// One wavefront per (sequence, query head); rows with one partition were
+// already written by the partition kernel.
+template <int D, class OutT>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (row >= (int64_t)a.num_seqs * a.num_q_heads) return;
+  const int seq = (int)(row / a.num_q_heads);
+  int L = a.lens[seq];
+  L = L < 0 ? 0 : L;
+  L = L > a.max_len ? a.max_len : L;
+  const int64_t cap = (int64_t)a.max_blocks * kBlock;
+  if ((int64_t)L > cap) L = (int)cap;
+  const int n_parts = (L + a.ps - 1) / a.ps;
+  if (n_parts <= 1) return;
+  const float* pm = a.part_m + row * a.num_parts;
+  const float* pl = a.part_l + row * a.num_parts;
+  float M = -INFINITY;
+  for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, pm[p]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  constexpr int PER = D / kWave;           // dims per lane: 1 or 2
+  float num[PER] = {};
+  float den = 0.f;
+  if (M != -INFINITY) {
+    for (int p = 0; p < n_parts; ++p) {
+      const float w = fast_exp2(pm[p] - M) * pl[p];
+      den += w;
+      const float* op = a.part_o + (row * a.num_parts + p) * D;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += w * op[lane + e * kWave];
+    }
+  }
+  OutT* o = reinterpret_cast<OutT*>(a.out) + row * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) store_out<OutT>(o + lane + e * kWave, den > 0.f ? num[e] / den : 0.f);
+}
+
+template <class Tag, int D, class OutT>
+static pa_status launch(const DecodeArgs& a, int64_t units, size_t lds, hipStream_t stream) {
+  decode_kernel<Tag, D, OutT><<<(unsigned)units, kThreads, lds, stream>>>(a);
+  pa_status st = launch_status();
+  if (st != PA_OK || a.num_parts <= 1) return st;
+  const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+  reduce_kernel<D, OutT><<<(unsigned)((rows + kWaves - 1) / kWaves), kThreads, 0, stream>>>(a);
+  return launch_status();
+}
+
+template <class Tag, class OutT>
+static pa_status dispatch_d(int D, const DecodeArgs& a, int64_t units, size_t lds, hipStream_t s) {
+  if (D == 128) return launch<Tag, 128, OutT>(a, units, lds, s);
+  return launch<Tag, 64, OutT>(a, units, lds, s);
+}
+
+// Partition geometry shared by the size query and the launch.
+static void geometry(int32_t max_len, int32_t partition_size, int32_t* ps, int32_t* parts) {
+  const int32_t whole = ((max_len > 0 ? max_len : 1) + kBlock - 1) / kBlock * kBlock;
+  *ps = partition_size == 0 ? whole : partition_size;
+  *parts = max_len > 0 ? (max_len + *ps - 1) / *ps : 1;
+}
+
+static size_t workspace_bytes(int64_t rows, int32_t parts, int32_t D) {
+  if (parts <= 1) return 0;
+  const int64_t ml = rows * parts * 4;                      // m and l, fp32
+  const int64_t ml_pad = (ml + 255) / 256 * 256;
+  return (size_t)(2 * ml_pad + rows * parts * (int64_t)D * 4);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_context_len,
+                                   int32_t partition_size, size_t* bytes) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (!bytes || num_seqs < 0 || num_q_heads < 1 || max_context_len < 0 || partition_size < 0)
+    return PA_ERR_INVALID_ARG;
+  if (partition_size % kBlock) return PA_ERR_INVALID_ARG;
+  int32_t ps, parts;
+  geometry(max_context_len, partition_size, &ps, &parts);
+  *bytes = workspace_bytes((int64_t)num_seqs * num_q_heads, parts, pool->head_dim);
+  return PA_OK;
+}
+
+pa_status pa_decode_attention(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
+                              const void* q, void* out, pa_dtype out_dtype,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, float scale, int32_t max_context_len,
+                              int32_t partition_size, void* workspace, size_t workspace_size,
+                              void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  if (G > 16) return PA_ERR_UNSUPPORTED;
+  if (partition_size % kBlock) return PA_ERR_INVALID_ARG;
+  if (out_dtype != PA_F32 && out_dtype != pool->dtype) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !out || !context_lens) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(q)) return PA_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PA_ERR_INVALID_ARG;
+
+  int32_t ps, parts;
+  geometry(max_context_len, partition_size, &ps, &parts);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  const size_t need = workspace_bytes(rows, parts, pool->head_dim);
+  if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+  const int64_t units = (int64_t)pool->num_kv_heads * num_seqs * parts;
+  if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
+
+  DecodeArgs a;
+  a.k_pool = (const char*)k_pool;
+  a.v_pool = (const char*)v_pool;
+  a.q = (const char*)q;
+  a.out = out;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.part_m = a.part_l = a.part_o = nullptr;
+  if (need > 0) {
+    const int64_t ml = rows * parts * 4;
+    const int64_t ml_pad = (ml + 255) / 256 * 256;
+    a.part_m = (float*)workspace;
+    a.part_l = (float*)((char*)workspace + ml_pad);
+    a.part_o = (float*)((char*)workspace + 2 * ml_pad);
+  }
+  a.num_blocks = pool->num_blocks;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = G;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_len = max_context_len;
+  a.ps = ps;
+  a.num_parts = parts;
+  a.qk_scale = scale * kLog2e;
+  const size_t lds = (size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float);
+  const hipStream_t s = (hipStream_t)stream;
+  const int D = pool->head_dim;
+
+  switch (pool->dtype) {
+    case PA_BF16:
+      return out_dtype == PA_F32 ? dispatch_d<TagBF16, float>(D, a, units, lds, s)
+                                 : dispatch_d<TagBF16, __bf16>(D, a, units, lds, s);
+    case PA_F16:
+      return out_dtype == PA_F32 ? dispatch_d<TagF16, float>(D, a, units, lds, s)
+                                 : dispatch_d<TagF16, _Float16>(D, a, units, lds, s);
+    case PA_F32:
+      return dispatch_d<TagF32, float>(D, a, units, lds, s);
+    default:
+      return PA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // extern "C"

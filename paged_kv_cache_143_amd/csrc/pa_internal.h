@@ -1,0 +1,47 @@
+// Internal helpers shared by the libpa HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;        // tokens per block (the only size built)
+constexpr int kWave = 64;         // CDNA wavefront width
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+inline int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+
+inline bool dtype_ok(pa_dtype t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
+
+// Host-side validation of a pool descriptor.  Returns PA_OK or the status.
+inline pa_status check_pool(const pa_pool_desc* p) {
+  if (!p) return PA_ERR_INVALID_ARG;
+  if (p->num_blocks < 1 || p->block_size < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
+    return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(p->dtype)) return PA_ERR_UNSUPPORTED;
+  if (p->block_size != kBlock) return PA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  // Flat slot indices are int32.
+  if ((int64_t)p->num_blocks * p->block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// Elements in one (block, KV head) tile and in one block across heads.
+inline int64_t tile_elems(const pa_pool_desc* p) { return (int64_t)p->block_size * p->head_dim; }
+
+inline pa_status launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+}  // namespace pa

@@ -1,0 +1,58 @@
+"""Helpers for GPU tests: device pool views in the documented layout, error metrics."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_143_amd import binding as B
+
+BLOCK = 16
+
+
+def announce(msg: str) -> None:
+    """Name the case on the real stderr before a GPU step (bypasses capture)."""
+    sys.__stderr__.write(f"[gpu] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    B.lib()                                   # raises if libpa.so is missing: no fallback
+    assert B.single_hip_runtime(), "two HIP runtimes are loaded"
+
+
+def pool_logical(kv, num_kv_heads: int, head_dim: int):
+    """Device pools -> fp64 CPU arrays [blocks][offset][head][dim], read through the
+    pool layout of include/pa.h (K: [d/X][b][X] tiles, V: [d][b] tiles)."""
+    es = kv.k.element_size()
+    X = 16 // es
+    nb = kv.k.numel() // (num_kv_heads * BLOCK * head_dim)
+    k = kv.k.view(nb, num_kv_heads, head_dim // X, BLOCK, X).permute(0, 3, 1, 2, 4)
+    k = k.reshape(nb, BLOCK, num_kv_heads, head_dim)
+    v = kv.v.view(nb, num_kv_heads, head_dim, BLOCK).permute(0, 3, 1, 2)
+    return (k.to(torch.float64).cpu().numpy(), v.to(torch.float64).cpu().numpy())
+
+
+def assert_pool_equal(got: np.ndarray, want: np.ndarray) -> None:
+    """Bit-level equality of values upcast from the pool dtype; NaN where unwritten."""
+    nan_w = np.isnan(want)
+    nan_g = np.isnan(got)
+    assert np.array_equal(nan_w, nan_g), f"{int((nan_w != nan_g).sum())} NaN positions differ"
+    diff = got[~nan_w] != want[~nan_w]
+    assert not diff.any(), f"{int(diff.sum())} elements differ"
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over (seq, head) rows of max_d |got - ref| / max_d |ref|."""
+    g = got.reshape(-1, got.shape[-1]).astype(np.float64)
+    r = ref.reshape(-1, ref.shape[-1]).astype(np.float64)
+    num = np.abs(g - r).max(axis=1)
+    den = np.abs(r).max(axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return float((num / den).max()) if len(num) else 0.0
+
+
+def tol_for(dtype: str) -> float:
+    return 1e-5 if dtype == "f32" else 2e-3
