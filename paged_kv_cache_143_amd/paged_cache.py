@@ -66,11 +66,16 @@ class Batch:
 
 
 class _Flusher:
-    """Accumulates writes and copies; flushes copies first, then writes."""
+    """Accumulates writes and copies; flushes copies first, then writes.
+
+    A flush happens before a copy whose source has a pending write or is a
+    pending copy's destination, and before a second write to a pending slot,
+    so every batched call is order-independent."""
 
     def __init__(self, w: Workload, kv: PagedKV, device: str, max_tokens: int = 1 << 16):
         self.w, self.kv, self.device, self.max_tokens = w, kv, device, max_tokens
         self.writes: List[Tuple[int, int, int]] = []      # (slot, key, row)
+        self.write_slots = set()
         self.write_blocks = set()
         self.pairs: List[Tuple[int, int]] = []
         self.copy_dsts = set()
@@ -78,7 +83,11 @@ class _Flusher:
         self.copy_calls = 0
 
     def add_write(self, slot: int, key: int, row: int) -> None:
+        # one call must not write a slot twice (which write lands is unspecified)
+        if slot in self.write_slots:
+            self.flush()
         self.writes.append((slot, key, row))
+        self.write_slots.add(slot)
         self.write_blocks.add(slot // BLOCK)
 
     def add_copy(self, src: int, dst: int) -> None:
@@ -95,7 +104,8 @@ class _Flusher:
         for a in range(0, len(self.writes), self.max_tokens):
             chunk = self.writes[a:a + self.max_tokens]
             self._write_chunk(chunk)
-        self.writes, self.write_blocks, self.pairs, self.copy_dsts = [], set(), [], set()
+        self.writes, self.write_slots, self.write_blocks = [], set(), set()
+        self.pairs, self.copy_dsts = [], set()
 
     def _write_chunk(self, chunk) -> None:
         arr = np.asarray(chunk, dtype=np.int64)
