@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+Workload: the batch-256 GQA decode layer -- 256 sequences with lengths
+uniform over 200..2000, 32 query / 8 KV heads of 128, bf16 pools of 16-token
+blocks on randomly permuted physical blocks (shapes of the pages' capacity
+exercise and of a GQA model; synthetic N(0,1) data, seed 3).
+
+One step = the whole decode hot path over the batch:
+  pa_slot_mapping (256 new tokens at positions L_i - 1)
+  -> pa_write_kv (their K/V into the pool)
+  -> pa_decode_attention (every sequence, every head, through its table).
+Inputs are resident in HBM before the timed region.  `value` is KV bytes
+read per step / step time (whole step); the roofline block reports the
+decode call alone, timed with HIP events on the stream it runs on.
+
+  python bench.py [--steps K] [--warmup W] [--partition P] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+DEFAULT_PARTITION = 0
+
+
+def _algorithmic_bytes(w, lens, partition):
+    """Bytes the decode call must move at minimum (each byte once)."""
+    import numpy as np
+    L = np.asarray(lens, dtype=np.int64)
+    es = 2 if w.dtype in ("bf16", "f16") else 4
+    kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * es
+    q = w.num_seqs * w.num_q_heads * w.head_dim * es
+    out = w.num_seqs * w.num_q_heads * w.head_dim * 4
+    tables = int(((L + 15) // 16).sum()) * 4 + w.num_seqs * 4
+    return {"kv": kv, "q": q, "out": out, "tables_lens": tables, "total": kv + q + out + tables}
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle (as it stands) on leading sequences of the same batch."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle.allocator import run_script
+    from oracle.attention import paged_decode
+    from oracle.pool import SlotPool
+
+    model = run_script(w.ops, w.num_blocks, w.block_size, w.free_order, checked=False)
+    pool = SlotPool(w.num_blocks, w.block_size)
+    pool.replay(model.events)
+    tables = [model.tables[n] for n in w.seq_names]
+    lens = [model.length(n) for n in w.seq_names]
+    q64 = w.queries().to(torch.float64).numpy()
+    elapsed, kv_bytes, done, tokens = 0.0, 0, 0, 0
+    with threadpool_limits(limits=1):
+        for i in range(w.num_seqs):
+            k, v = w.kv(w.seq_names[i])
+            cache = (k.to(torch.float64).numpy(), v.to(torch.float64).numpy())
+            resolve = lambda p, c=cache: (c[0][p[1]], c[1][p[1]])
+            t0 = time.perf_counter()
+            paged_decode(pool, resolve, tables, lens, q64, w.num_kv_heads, w.scale, rows=[i])
+            elapsed += time.perf_counter() - t0
+            w.drop_cache()
+            kv_bytes += lens[i] * w.num_kv_heads * w.head_dim * 2 * 2
+            tokens += lens[i]
+            done += 1
+            if elapsed >= budget_s:
+                break
+    return {"value": kv_bytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {w.num_seqs} sequences ({tokens} context tokens, all "
+                      f"{w.num_q_heads} query heads), fp64 NumPy oracle, 1 thread, "
+                      f"{elapsed:.1f} s",
+            "seconds": elapsed, "sequences": done}
+
+
+def run(args):
+    import numpy as np
+    import torch
+    from paged_kv_cache_143_amd import binding
+    from paged_kv_cache_143_amd import workloads as W
+    from paged_kv_cache_143_amd.paged_cache import DecodeStep, build_batch
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    binding.lib()
+    torch.cuda.set_device(0)
+    w = W.gqa_bf16()
+    t_setup = time.perf_counter()
+    batch = build_batch(w, device="cuda")
+    lens = batch.bm.length_array(w.seq_names)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print(f"[bench] setup {setup_s:.1f}s: {w.name}, {int(lens.sum())} context tokens, "
+          f"{w.num_blocks} blocks", file=sys.stderr, flush=True)
+
+    results = {}
+    partitions = args.sweep if args.sweep else [args.partition]
+    for ps in partitions:
+        step = DecodeStep(batch, partition_size=ps)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1, e2 in ev:
+            e0.record()
+            step.write_current()
+            e1.record()
+            step.attend()
+            e2.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        write_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+        dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+        results[ps] = (wall / args.steps * 1e3, write_ms, dec_ms)
+        print(f"[bench] partition {ps}: step {wall / args.steps * 1e3:.4f} ms, decode call "
+              f"median {np.median(dec_ms) * 1e3:.1f} us, write+slots median "
+              f"{np.median(write_ms) * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    ps = partitions[0] if not args.sweep else min(results, key=lambda p: results[p][0])
+    ms_step, write_ms, dec_ms = results[ps]
+    alg = _algorithmic_bytes(w, lens, ps)
+    dec_mean_s = float(dec_ms.mean()) / 1e3
+    achieved = alg["total"] / dec_mean_s / 1e9
+    kv_gbs = alg["kv"] / (ms_step / 1e3) / 1e9
+    line = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) + tokens/s at batch 256, 1 GPU",
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gqa-bf16-b256", "num_seqs": w.num_seqs,
+                   "lengths": "uniform int 200..2000", "context_tokens": int(lens.sum()),
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "partition_size": ps, "out_dtype": "f32", "seed": w.seed,
+                   "step": "slot_mapping + write_kv(256 tokens) + decode_attention"},
+        "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.num_seqs / (ms_step / 1e3), 1),
+        "context_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
+        "kernels_us": {"write_and_slots_median": round(float(np.median(write_ms)) * 1e3, 2),
+                       "decode_call_median": round(float(np.median(dec_ms)) * 1e3, 2),
+                       "decode_call_mean": round(dec_mean_s * 1e6, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "pa_decode_attention (decode_kernel"
+                     + (" + reduce_kernel" if ps and ps < int(lens.max()) else "") + ")",
+                     "algorithmic_bytes": alg},
+    }
+    if args.sweep:
+        line["sweep_ms_per_step"] = {str(p): round(v[0], 5) for p, v in results.items()}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W.gqa_bf16(), args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition", type=int, default=DEFAULT_PARTITION,
+                    help="partition size in tokens (0 = one work unit per sequence and KV head)")
+    ap.add_argument("--sweep", type=int, nargs="*", default=None,
+                    help="time several partition sizes and report the fastest")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work in the CPU baseline sample")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the decode path here is built and timed on a "
+              "single MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,5 +9,7 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    from tests import gpu_util
+    gpu_util.set_config(config)
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: large CPU oracle runs")

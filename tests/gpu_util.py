@@ -10,10 +10,23 @@ from paged_kv_cache_143_amd import binding as B
 BLOCK = 16
 
 
+_CONFIG = None
+
+
+def set_config(config) -> None:
+    global _CONFIG
+    _CONFIG = config
+
+
 def announce(msg: str) -> None:
-    """Name the case on the real stderr before a GPU step (bypasses capture)."""
-    sys.__stderr__.write(f"[gpu] {msg}\n")
-    sys.__stderr__.flush()
+    """Print (uncaptured, flushed) the case name before a GPU step."""
+    capman = _CONFIG.pluginmanager.getplugin("capturemanager") if _CONFIG else None
+    if capman is not None:
+        with capman.global_and_fixture_disabled():
+            print(f"[gpu] {msg}", flush=True)
+    else:
+        sys.__stderr__.write(f"[gpu] {msg}\n")
+        sys.__stderr__.flush()
 
 
 def require_gpu():
