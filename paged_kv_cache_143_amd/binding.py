@@ -53,13 +53,18 @@ def _hip_runtimes_loaded():
 def lib() -> ctypes.CDLL:
     """Load libpa.so once (after torch, so both share torch's HIP runtime)."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a libpa build and declare its entry points."""
     import torch  # noqa: F401  -- loads the HIP runtime torch was built with
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m paged_kv_cache_143_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_status_string.argtypes = [I32]
     L.pa_version.restype = I32
@@ -78,7 +83,6 @@ def lib() -> ctypes.CDLL:
                                       I32, I32, ctypes.c_float, I32, I32, P, ctypes.c_size_t, P]
     L.pa_validate_tables.restype = I32
     L.pa_validate_tables.argtypes = [ctypes.POINTER(PoolDesc), P, I32, P, I32, I32, P, P]
-    _lib = L
     return L
 
 

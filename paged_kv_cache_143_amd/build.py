@@ -32,10 +32,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; libpa.so cannot be built")
 
 
-def build(verbose: bool = True, extra_flags=()) -> str:
-    """Compile every HIP source into paged_kv_cache_143_amd/libpa.so; returns its path."""
+def build(verbose: bool = True, extra_flags=(), out: str = LIB) -> str:
+    """Compile every HIP source into `out` (default paged_kv_cache_143_amd/libpa.so)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
     if verbose:
         print("[build]", " ".join(cmd), flush=True)
@@ -47,8 +47,8 @@ def build(verbose: bool = True, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -35,7 +35,13 @@
 // workspace and a reduce kernel rescales them by exp2(m_p - max m).
 //
 // fp32 pools use v_mfma_f32_16x16x4_f32 in the same roles (one k per lane).
+#include <algorithm>
+
 #include "pa_internal.h"
+
+#ifndef PA_TEMPORAL_KV
+#define PA_TEMPORAL_KV 0
+#endif
 
 namespace pa {
 
@@ -69,8 +75,35 @@ struct DecodeArgs {
   int32_t max_len;     // clip for lengths
   int32_t ps;          // partition size in tokens (multiple of 16)
   int32_t num_parts;   // P = ceil(max_len / ps)
+  int32_t longest_first;  // 1: map workgroups to sequences in decreasing length
   float qk_scale;      // scale * log2(e)
 };
+
+// Longest-first dispatch.  Workgroups start roughly in blockIdx order, so
+// giving consecutive indices to sequences in decreasing length (longest
+// processing time first) keeps the last workgroups to finish short.  Each
+// workgroup ranks the lengths itself, with unique keys (length, then lower
+// index first): rank(i) = #{j : key_j > key_i}.  O(S^2 / threads) compares.
+constexpr int kRankMax = 512;
+
+__device__ inline int seq_of_rank(const int32_t* __restrict__ lens, int S, int r, uint32_t* keys) {
+  for (int i = threadIdx.x; i < S; i += blockDim.x) {
+    int L = lens[i];
+    L = L < 0 ? 0 : (L > (1 << 20) - 1 ? (1 << 20) - 1 : L);
+    keys[i] = ((uint32_t)L << 11) | (uint32_t)(2047 - i);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < S; i += blockDim.x) {
+    const uint32_t ki = keys[i];
+    int rank = 0;
+    for (int j = 0; j < S; ++j) rank += keys[j] > ki ? 1 : 0;
+    if (rank == r) keys[kRankMax] = (uint32_t)i;
+  }
+  __syncthreads();
+  const int seq = (int)keys[kRankMax];
+  __syncthreads();                             // the keys area is reused afterwards
+  return seq;
+}
 
 // ---- matrix-core wrappers -------------------------------------------------
 template <class Tag> __device__ inline f32x4 mma32(u32x4 a, u32x4 b, f32x4 c);
@@ -121,6 +154,15 @@ __device__ inline float xor_sum(float v) {
 // the 4 tokens 4*(lane/16) ...
 template <class Tag, int D, bool H = Is16<Tag>::value> struct Frag;
 
+// KV tiles are read exactly once per call: streaming (non-temporal) loads.
+template <class T> __device__ inline T stream_load(const char* p) {
+#if PA_TEMPORAL_KV
+  return *reinterpret_cast<const T*>(p);
+#else
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+#endif
+}
+
 template <class Tag, int D> struct Frag<Tag, D, true> {
   static constexpr int NK = D / 32;
   static constexpr int NV = D / 16;
@@ -128,12 +170,10 @@ template <class Tag, int D> struct Frag<Tag, D, true> {
   u32x2 v[NV];
   __device__ inline void load(const char* kt, const char* vt, int lane) {
 #pragma unroll
-    for (int m = 0; m < NK; ++m)
-      k[m] = *reinterpret_cast<const u32x4*>(kt + m * 1024 + lane * 16);
+    for (int m = 0; m < NK; ++m) k[m] = stream_load<u32x4>(kt + m * 1024 + lane * 16);
     const int off = (lane & 15) * 32 + (lane >> 4) * 8;
 #pragma unroll
-    for (int n = 0; n < NV; ++n)
-      v[n] = *reinterpret_cast<const u32x2*>(vt + n * 512 + off);
+    for (int n = 0; n < NV; ++n) v[n] = stream_load<u32x2>(vt + n * 512 + off);
   }
 };
 
@@ -147,12 +187,10 @@ template <class Tag, int D> struct Frag<Tag, D, false> {
   f32x4 v[NV];
   __device__ inline void load(const char* kt, const char* vt, int lane) {
 #pragma unroll
-    for (int j = 0; j < NK; ++j)
-      k[j] = *reinterpret_cast<const f32x4*>(kt + j * 1024 + lane * 16);
+    for (int j = 0; j < NK; ++j) k[j] = stream_load<f32x4>(kt + j * 1024 + lane * 16);
     const int off = (lane & 15) * 64 + (lane >> 4) * 16;
 #pragma unroll
-    for (int n = 0; n < NV; ++n)
-      v[n] = *reinterpret_cast<const f32x4*>(vt + n * 1024 + off);
+    for (int n = 0; n < NV; ++n) v[n] = stream_load<f32x4>(vt + n * 1024 + off);
   }
 };
 
@@ -264,8 +302,13 @@ template <class Tag> struct Elt { using T = uint16_t; static constexpr int bytes
 template <> struct Elt<TagF32> { using T = float; static constexpr int bytes = 4; };
 
 // One workgroup per (KV head, sequence, partition); see the file comment.
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 3
+#endif
+
 template <class Tag, int D, class OutT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+void decode_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   constexpr int ES = Elt<Tag>::bytes;
   constexpr int64_t kTileBytes = (int64_t)kBlock * D * ES;
@@ -276,8 +319,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int g = unit % a.num_kv_heads;
   const int rest = unit / a.num_kv_heads;
-  const int seq = rest % a.num_seqs;
   const int part = rest / a.num_seqs;
+  const int seq = a.longest_first
+                      ? seq_of_rank(a.lens, a.num_seqs, rest % a.num_seqs,
+                                    reinterpret_cast<uint32_t*>(smem))
+                      : rest % a.num_seqs;
 
   int L = a.lens[seq];
   L = L < 0 ? 0 : L;
@@ -337,20 +383,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const int64_t off = (int64_t)phys_of(i, nv) * block_stride + head_tile;
       f.load(a.k_pool + off, a.v_pool + off, lane);
     };
+    // Loads are unconditional so that every computation waits only for its own
+    // block (a conditional load makes the wait counts path-dependent and the
+    // compiler falls back to waiting for everything).  Past the last block the
+    // index is clamped: the spare load re-reads a block the wavefront just
+    // fetched.
     load_into(fa, 0, nva);
-    int i = 0;
-    for (; i + 2 < n; i += 2) {
-      load_into(fb, i + 1, nvb);
+    for (int i = 0; i < n; i += 2) {
+      load_into(fb, min(i + 1, n - 1), nvb);
       if (nva > 0) attend_block<Tag, D>(fa, qf, st, nva, a.qk_scale, lane);
-      load_into(fa, i + 2, nva);
+      if (i + 1 >= n) break;
+      load_into(fa, min(i + 2, n - 1), nva);
       if (nvb > 0) attend_block<Tag, D>(fb, qf, st, nvb, a.qk_scale, lane);
-    }
-    if (i + 1 < n) {
-      load_into(fb, i + 1, nvb);
-      if (nva > 0) attend_block<Tag, D>(fa, qf, st, nva, a.qk_scale, lane);
-      if (nvb > 0) attend_block<Tag, D>(fb, qf, st, nvb, a.qk_scale, lane);
-    } else {
-      if (nva > 0) attend_block<Tag, D>(fa, qf, st, nva, a.qk_scale, lane);
     }
   }
 
@@ -547,8 +591,10 @@ pa_status pa_decode_attention(const pa_pool_desc* pool, const void* k_pool, cons
   a.max_len = max_context_len;
   a.ps = ps;
   a.num_parts = parts;
+  a.longest_first = num_seqs <= kRankMax ? 1 : 0;
   a.qk_scale = scale * kLog2e;
-  const size_t lds = (size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float);
+  size_t lds = (size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float);
+  if (a.longest_first) lds = std::max(lds, (size_t)(kRankMax + 1) * sizeof(uint32_t));
   const hipStream_t s = (hipStream_t)stream;
   const int D = pool->head_dim;
 
