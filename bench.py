@@ -6,15 +6,18 @@ uniform over 200..2000, 32 query / 8 KV heads of 128, bf16 pools of 16-token
 blocks on randomly permuted physical blocks (shapes of the pages' capacity
 exercise and of a GQA model; synthetic N(0,1) data, seed 3).
 
-One step = the whole decode hot path over the batch:
-  pa_slot_mapping (256 new tokens at positions L_i - 1)
-  -> pa_write_kv (their K/V into the pool)
-  -> pa_decode_attention (every sequence, every head, through its table).
-Inputs are resident in HBM before the timed region.  `value` is KV bytes
-read per step / step time (whole step); the roofline block reports the
-decode call alone, timed with HIP events on the stream it runs on.
+One step = the whole decode hot path over the batch: address translation of
+the 256 current tokens (positions L_i - 1), their K/V written into the pool,
+and decode attention for every sequence and head through its table.  By
+default this is one pa_decode_step launch (slot computed in-kernel, write
+fused, the written token patched into registers); --unfused issues
+pa_slot_mapping + pa_write_kv + pa_decode_attention instead.  Inputs are
+resident in HBM before the timed region.  `value` is KV bytes read per step /
+step time (whole step); the roofline block reports the launch that reads the
+KV (the fused step, or the decode call), timed with HIP events on the stream
+it runs on.
 
-  python bench.py [--steps K] [--warmup W] [--partition P] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--partition P] [--unfused] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -32,8 +35,11 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 DEFAULT_PARTITION = 0
 
 
-def _algorithmic_bytes(w, lens, partition):
-    """Bytes the decode call must move at minimum (each byte once)."""
+def _algorithmic_bytes(w, lens, fused):
+    """Bytes the KV-reading launch must move at minimum (each byte once): the
+    KV of every valid (token, KV head) -- 2 * head_dim * 2 B = 512 B each for
+    bf16 -- plus q, out, tables and lengths, plus (fused step) the current
+    tokens' K/V read from k_new/v_new and written to the pool."""
     import numpy as np
     L = np.asarray(lens, dtype=np.int64)
     es = 2 if w.dtype in ("bf16", "f16") else 4
@@ -41,7 +47,9 @@ def _algorithmic_bytes(w, lens, partition):
     q = w.num_seqs * w.num_q_heads * w.head_dim * es
     out = w.num_seqs * w.num_q_heads * w.head_dim * 4
     tables = int(((L + 15) // 16).sum()) * 4 + w.num_seqs * 4
-    return {"kv": kv, "q": q, "out": out, "tables_lens": tables, "total": kv + q + out + tables}
+    new = 2 * (w.num_seqs * w.num_kv_heads * w.head_dim * 2 * es) if fused else 0
+    return {"kv": kv, "q": q, "out": out, "tables_lens": tables, "new_tokens": new,
+            "total": kv + q + out + tables + new}
 
 
 def cpu_baseline(w, budget_s: float):
@@ -104,7 +112,7 @@ def run(args):
     results = {}
     partitions = args.sweep if args.sweep else [args.partition]
     for ps in partitions:
-        step = DecodeStep(batch, partition_size=ps)
+        step = DecodeStep(batch, partition_size=ps, fused=not args.unfused)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -114,22 +122,27 @@ def run(args):
         t0 = time.perf_counter()
         for e0, e1, e2 in ev:
             e0.record()
-            step.write_current()
-            e1.record()
-            step.attend()
+            if not args.unfused:
+                e1.record()
+                step.fused_step()
+            else:
+                step.write_current()
+                e1.record()
+                step.attend()
             e2.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         write_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
         dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
         results[ps] = (wall / args.steps * 1e3, write_ms, dec_ms)
-        print(f"[bench] partition {ps}: step {wall / args.steps * 1e3:.4f} ms, decode call "
-              f"median {np.median(dec_ms) * 1e3:.1f} us, write+slots median "
+        print(f"[bench] partition {ps}{' unfused' if args.unfused else ''}: step "
+              f"{wall / args.steps * 1e3:.4f} ms, KV-reading launch median "
+              f"{np.median(dec_ms) * 1e3:.1f} us, separate write+slots median "
               f"{np.median(write_ms) * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     ps = partitions[0] if not args.sweep else min(results, key=lambda p: results[p][0])
     ms_step, write_ms, dec_ms = results[ps]
-    alg = _algorithmic_bytes(w, lens, ps)
+    alg = _algorithmic_bytes(w, lens, not args.unfused)
     dec_mean_s = float(dec_ms.mean()) / 1e3
     achieved = alg["total"] / dec_mean_s / 1e9
     kv_gbs = alg["kv"] / (ms_step / 1e3) / 1e9
@@ -151,17 +164,22 @@ def run(args):
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "partition_size": ps, "out_dtype": "f32", "seed": w.seed,
-                   "step": "slot_mapping + write_kv(256 tokens) + decode_attention"},
+                   "step": ("pa_slot_mapping + pa_write_kv(256 tokens) + pa_decode_attention"
+                            if args.unfused else
+                            "pa_decode_step (slot + write of 256 tokens + decode, one launch)")},
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.num_seqs / (ms_step / 1e3), 1),
         "context_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
-        "kernels_us": {"write_and_slots_median": round(float(np.median(write_ms)) * 1e3, 2),
-                       "decode_call_median": round(float(np.median(dec_ms)) * 1e3, 2),
-                       "decode_call_mean": round(dec_mean_s * 1e6, 2)},
+        "kernels_us": {"separate_write_and_slots_median":
+                           round(float(np.median(write_ms)) * 1e3, 2) if args.unfused else 0.0,
+                       "kv_launch_median": round(float(np.median(dec_ms)) * 1e3, 2),
+                       "kv_launch_mean": round(dec_mean_s * 1e6, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "pa_decode_attention (decode_kernel"
-                     + (" + reduce_kernel" if ps and ps < int(lens.max()) else "") + ")",
+                     "traffic": None,
+                     "kernel": ("pa_decode_attention" if args.unfused else "pa_decode_step")
+                     + " (decode_kernel" + (" + reduce_kernel" if ps and ps < int(lens.max())
+                                            else "") + ")",
                      "algorithmic_bytes": alg},
     }
     if args.sweep:
@@ -180,6 +198,8 @@ def main():
                     help="partition size in tokens (0 = one work unit per sequence and KV head)")
     ap.add_argument("--sweep", type=int, nargs="*", default=None,
                     help="time several partition sizes and report the fastest")
+    ap.add_argument("--unfused", action="store_true",
+                    help="three launches per step instead of pa_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work in the CPU baseline sample")

@@ -52,13 +52,15 @@
  *   block_size * head_dim elements; tile (blk, h) starts at element
  *   (blk * Hkv + h) * block_size * head_dim, so every (block, KV head) tile is
  *   one contiguous 4 KiB run for 16 x 128 16-bit or 16 x 64 fp32 elements.
- *   Inside a tile, with X = 16 / sizeof(element) (8 for f16/bf16, 4 for f32):
- *     K: element (offset o, dim d) at ((d / X) * block_size + o) * X + d % X
- *        -- 16-byte vectors of X consecutive dims, token-major within a
- *        vector column ("[d/X][b][X]");
- *     V: element (offset o, dim d) at d * block_size + o
- *        -- transposed, tokens contiguous per dim ("[d][b]").
- *   Both make the decode kernel's per-instruction loads one contiguous run.
+ *   Inside a tile:
+ *     K: element (offset o, dim d) at o * head_dim + d
+ *        -- token-major: one token's K is one contiguous row;
+ *     V: element (offset o, dim d) at ((o / 4) * head_dim + d) * 4 + o % 4
+ *        -- groups of 4 tokens interleaved per dim ("[b/4][d][4]").
+ *   The decode kernel reads both with full 128-byte lines per instruction,
+ *   each lane receiving its matrix-core operand directly (a token's 8 dims of
+ *   K; 4 consecutive tokens of one dim of V), and a token write touches
+ *   2 lines of K and 8 lines of V for 128 16-bit dims.
  *
  * Supported shapes: block_size 16; head_dim 64 or 128; dtype f32, f16, bf16;
  * 1 <= num_q_heads / num_kv_heads <= 16 and num_q_heads % num_kv_heads == 0.
@@ -194,6 +196,34 @@ PA_API pa_status pa_decode_attention(const pa_pool_desc* pool, const void* k_poo
                               int32_t num_q_heads, float scale, int32_t max_context_len,
                               int32_t partition_size, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * pa_decode_step -- one decode iteration in one launch: for every sequence i
+ * with L_i >= 1, write row i of k_new / v_new (its current token) to
+ * position L_i - 1, i.e. slot table[i][(L_i-1)/b]*b + (L_i-1)%b, then
+ * attend over positions 0 .. L_i - 1 exactly as pa_decode_attention does.
+ * Same result as pa_slot_mapping + pa_write_kv + pa_decode_attention with
+ * those positions (the growth step of "Inside vLLM and TGI", section "Exact
+ * CPU block manager and copy-on-write", followed by the attention step of the
+ * transcript, paragraph 3).  The last block must already be private to the
+ * sequence (copy-on-write done).
+ *   k_pool, v_pool   device, pool layout above (one slot per sequence written)
+ *   k_new, v_new     device, pool dtype; sequence i, KV head h, dim d at
+ *                    element i * new_stride + h * head_dim + d
+ *   new_stride       elements between sequences (>= Hkv * head_dim, 16-byte
+ *                    multiple)
+ *   other arguments as pa_decode_attention.  A table entry outside the pool
+ *   for the current token's block: nothing is written and that block
+ *   contributes no tokens.
+ */
+PA_API pa_status pa_decode_step(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                                const void* k_new, const void* v_new, int64_t new_stride,
+                                const void* q, void* out, pa_dtype out_dtype,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, float scale, int32_t max_context_len,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * pa_validate_tables -- debug check of device-resident tables before a

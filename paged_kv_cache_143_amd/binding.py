@@ -21,7 +21,7 @@ DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_attention",
-           "pa_validate_tables")
+           "pa_decode_step", "pa_validate_tables")
 
 
 class PaError(RuntimeError):
@@ -81,6 +81,10 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_attention.restype = I32
     L.pa_decode_attention.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I32, P, I32, P,
                                       I32, I32, ctypes.c_float, I32, I32, P, ctypes.c_size_t, P]
+    if hasattr(L, "pa_decode_step"):          # absent from builds older than the fused step
+        L.pa_decode_step.restype = I32
+        L.pa_decode_step.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I64, P, P, I32, P, I32,
+                                     P, I32, I32, ctypes.c_float, I32, I32, P, ctypes.c_size_t, P]
     L.pa_validate_tables.restype = I32
     L.pa_validate_tables.argtypes = [ctypes.POINTER(PoolDesc), P, I32, P, I32, I32, P, P]
     return L
@@ -136,6 +140,15 @@ def pa_decode_attention(desc, k_pool, v_pool, q, out, out_dtype, block_tables,
                                      block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                      num_q_heads, scale, max_context_len, partition_size,
                                      workspace, workspace_bytes, stream)
+
+
+def pa_decode_step(desc, k_pool, v_pool, k_new, v_new, new_stride, q, out, out_dtype,
+                   block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
+                   max_context_len, partition_size, workspace, workspace_bytes, stream) -> int:
+    return lib().pa_decode_step(ctypes.byref(desc), k_pool, v_pool, k_new, v_new, new_stride, q,
+                                out, out_dtype, block_tables, max_blocks_per_seq, context_lens,
+                                num_seqs, num_q_heads, scale, max_context_len, partition_size,
+                                workspace, workspace_bytes, stream)
 
 
 def pa_validate_tables(desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
@@ -219,6 +232,28 @@ def decode_attention_t(desc, k_pool, v_pool, q, out, block_tables, context_lens,
                                _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
                                S, Hq, float(scale), int(max_context_len), int(partition_size),
                                _ptr(workspace), ws_bytes, _stream()))
+
+
+def decode_step_t(desc, k_pool, v_pool, k_new, v_new, q, out, block_tables, context_lens, scale,
+                  max_context_len, partition_size=0, workspace=None) -> None:
+    import torch
+    _dev_i32(block_tables, "block_tables")
+    _dev_i32(context_lens, "context_lens")
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    if k_new.stride() != v_new.stride() or k_new.stride(-1) != 1:
+        raise ValueError("k_new and v_new must share a row stride with contiguous dims")
+    S, Hq, D = q.shape
+    if k_new.shape[0] != S or v_new.shape[0] != S:
+        raise ValueError("k_new / v_new need one row per sequence")
+    out_code = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[out.dtype]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_step",
+           pa_decode_step(desc, _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                          k_new.stride(0), _ptr(q), _ptr(out), out_code, _ptr(block_tables),
+                          block_tables.shape[1], _ptr(context_lens), S, Hq, float(scale),
+                          int(max_context_len), int(partition_size), _ptr(workspace), ws_bytes,
+                          _stream()))
 
 
 def validate_tables_t(desc, block_tables, context_lens, max_context_len, bad_count) -> None:

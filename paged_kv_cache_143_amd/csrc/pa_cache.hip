@@ -37,8 +37,9 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t 
 
 // ---------------------------------------------------------------------------
 // Token writes.  One thread moves one 16-byte vector of X consecutive dims of
-// one (token, KV head).  K goes to the [d/X][b][X] tile as one 16-byte store;
-// V goes to the transposed [d][b] tile as X element stores (stride b).
+// one (token, KV head).  K tiles are token-major ([16][d]): the vector is one
+// 16-byte store and a token's row is contiguous.  V tiles interleave groups of
+// 4 tokens per dim ([16/4][d][4]): X element stores, stride 4 elements.
 // ---------------------------------------------------------------------------
 template <int ES>  // element size in bytes: 2 or 4
 __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
@@ -60,20 +61,18 @@ __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_
   const int32_t off = slot - blk * kBlock;
   const int64_t src = ((int64_t)t * new_stride + (int64_t)h * head_dim + (int64_t)c * X) * ES;
   const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)kBlock * head_dim;   // elements
-  // K: vector column c, row `off`.
   const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + src);
-  *reinterpret_cast<u32x4*>(k_pool + (tile + ((int64_t)c * kBlock + off) * X) * ES) = kv;
-  // V: dims c*X .. c*X+X-1 of token `off`, transposed.
+  *reinterpret_cast<u32x4*>(k_pool + (tile + (int64_t)off * head_dim + (int64_t)c * X) * ES) = kv;
   const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + src);
-  char* vt = v_pool + (tile + (int64_t)c * X * kBlock + off) * ES;
+  char* vb = v_pool + (tile + ((int64_t)(off >> 2) * head_dim + (int64_t)c * X) * 4 + (off & 3)) * ES;
   if constexpr (ES == 4) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vt + (int64_t)e * kBlock * 4) = vv[e];
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vb + (int64_t)e * 4 * 4) = vv[e];
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint16_t half = (uint16_t)(vv[e >> 1] >> ((e & 1) * 16));
-      *reinterpret_cast<uint16_t*>(vt + (int64_t)e * kBlock * 2) = half;
+      *reinterpret_cast<uint16_t*>(vb + (int64_t)e * 4 * 2) = half;
     }
   }
 }

@@ -45,7 +45,10 @@
 
 namespace pa {
 
-constexpr int kWaves = 4;
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+constexpr int kWaves = PA_WAVES;
 constexpr int kThreads = kWave * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -57,8 +60,12 @@ template <class Tag> struct Is16 { static constexpr bool value = true; };
 template <> struct Is16<TagF32> { static constexpr bool value = false; };
 
 struct DecodeArgs {
-  const char* k_pool;
-  const char* v_pool;
+  char* k_pool;        // written only by the fused step (the current token)
+  char* v_pool;
+  const char* k_new;   // fused step: current token's K/V per sequence, else null
+  const char* v_new;
+  int64_t new_stride;  // elements between sequences in k_new / v_new
+  int32_t stage_off;   // LDS byte offset of the staged current token
   const char* q;
   void* out;
   const int32_t* tables;
@@ -149,9 +156,10 @@ __device__ inline float xor_sum(float v) {
 }
 
 // ---- per-block register fragments ------------------------------------------
-// 16-bit: K tile [d/8][16][8] -> load m gives lane (t = lane%16) the 8 dims
-// 8*(4m + lane/16) ..; V tile [d][16] -> load n gives lane (d = 16n + lane%16)
-// the 4 tokens 4*(lane/16) ...
+// 16-bit: K tile [16][d] -> load m gives lane (t = lane%16) the 8 dims
+// 8*(4m + lane/16) .. of its token (16 bytes); V tile [16/4][d][4] -> load n
+// gives lane (d = 16n + lane%16) the 4 tokens 4*(lane/16) .. of that dim
+// (8 bytes; each instruction reads four full 128-byte lines).
 template <class Tag, int D, bool H = Is16<Tag>::value> struct Frag;
 
 // KV tiles are read exactly once per call: streaming (non-temporal) loads.
@@ -169,28 +177,30 @@ template <class Tag, int D> struct Frag<Tag, D, true> {
   u32x4 k[NK];
   u32x2 v[NV];
   __device__ inline void load(const char* kt, const char* vt, int lane) {
+    const char* kr = kt + (lane & 15) * (D * 2) + (lane >> 4) * 16;
 #pragma unroll
-    for (int m = 0; m < NK; ++m) k[m] = stream_load<u32x4>(kt + m * 1024 + lane * 16);
-    const int off = (lane & 15) * 32 + (lane >> 4) * 8;
+    for (int m = 0; m < NK; ++m) k[m] = stream_load<u32x4>(kr + m * 64);
+    const char* vr = vt + (lane >> 4) * (D * 8) + (lane & 15) * 8;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) v[n] = stream_load<u32x2>(vt + n * 512 + off);
+    for (int n = 0; n < NV; ++n) v[n] = stream_load<u32x2>(vr + n * 128);
   }
 };
 
-// fp32: K tile [d/4][16][4] -> load j gives lane (t = lane%16) dims
-// 4*(4j + lane/16) ..; V tile [d][16] -> load n gives lane (d = 16n + lane%16)
-// the 4 tokens 4*(lane/16) ...
+// fp32: K tile [16][d] -> load j gives lane (t = lane%16) dims
+// 4*(4j + lane/16) ..; V tile [16/4][d][4] -> load n gives lane
+// (d = 16n + lane%16) the 4 tokens 4*(lane/16) ...
 template <class Tag, int D> struct Frag<Tag, D, false> {
   static constexpr int NK = D / 16;
   static constexpr int NV = D / 16;
   f32x4 k[NK];
   f32x4 v[NV];
   __device__ inline void load(const char* kt, const char* vt, int lane) {
+    const char* kr = kt + (lane & 15) * (D * 4) + (lane >> 4) * 16;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) k[j] = stream_load<f32x4>(kt + j * 1024 + lane * 16);
-    const int off = (lane & 15) * 64 + (lane >> 4) * 16;
+    for (int j = 0; j < NK; ++j) k[j] = stream_load<f32x4>(kr + j * 64);
+    const char* vr = vt + (lane >> 4) * (D * 16) + (lane & 15) * 16;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) v[n] = stream_load<f32x4>(vt + n * 1024 + off);
+    for (int n = 0; n < NV; ++n) v[n] = stream_load<f32x4>(vr + n * 256);
   }
 };
 
@@ -215,6 +225,109 @@ template <class Tag, int D> struct QFrag<Tag, D, false> {
       q[j] = valid ? *reinterpret_cast<const f32x4*>(qrow + dim0 * 4) : f32x4{0, 0, 0, 0};
     }
   }
+};
+
+// The fused step writes the current token (offset o of its block) to the pool
+// and, for the one block that holds it, replaces the loaded values of that
+// token with the staged copy -- the tile load may have raced the store.
+template <class Tag, int D>
+__device__ inline void patch_token(Frag<Tag, D, true>& f, const char* stage, int o, int lane) {
+  if ((lane & 15) == o) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+      f.k[m] = *reinterpret_cast<const u32x4*>(stage + (4 * m + (lane >> 4)) * 16);
+  }
+  // Element indices below are runtime values: select, never index registers
+  // dynamically (that would move the fragment to scratch memory).
+  if ((lane >> 4) == (o >> 2)) {
+    const int dl = lane & 15;
+    const int shift = (o & 1) * 16;
+    const uint32_t keep = ~(0xffffu << shift);
+    const bool second = (o & 2) != 0;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const uint32_t val = *reinterpret_cast<const uint16_t*>(stage + D * 2 + (16 * n + dl) * 2);
+      const uint32_t w0 = f.v[n][0], w1 = f.v[n][1];
+      f.v[n][0] = second ? w0 : (w0 & keep) | (val << shift);
+      f.v[n][1] = second ? (w1 & keep) | (val << shift) : w1;
+    }
+  }
+}
+template <class Tag, int D>
+__device__ inline void patch_token(Frag<Tag, D, false>& f, const char* stage, int o, int lane) {
+  if ((lane & 15) == o) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      f.k[j] = *reinterpret_cast<const f32x4*>(stage + (4 * j + (lane >> 4)) * 16);
+  }
+  if ((lane >> 4) == (o >> 2)) {
+    const int dl = lane & 15;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const float val = *reinterpret_cast<const float*>(stage + D * 4 + (16 * n + dl) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f.v[n][e] = (e == (o & 3)) ? val : f.v[n][e];
+    }
+  }
+}
+
+// The current token's K/V for KV head g: loaded into registers when the
+// workgroup starts (one 16-byte vector per thread), staged in LDS once the
+// first blocks are in flight (for patch_token), and stored to its slot after
+// the block loop -- K as 16-byte vectors of the token's contiguous row (two
+// 128-byte lines for 128 bf16 dims), V as elements interleaved by 4 tokens
+// (eight lines).  Writes cost per line touched while reads stream.
+template <class Tag, int D> struct NewToken {
+  static constexpr int ES = Is16<Tag>::value ? 2 : 4;
+  static constexpr int X = 16 / ES;
+  static constexpr int NC = D / X;            // 16-byte vectors per head row
+  u32x4 vec;
+
+  __device__ inline void load(const DecodeArgs& a, int seq, int g) {
+    const int t = threadIdx.x;
+    if (t < 2 * NC) {
+      const bool is_v = t >= NC;
+      const int c = is_v ? t - NC : t;
+      const char* src = (is_v ? a.v_new : a.k_new) +
+                        ((int64_t)seq * a.new_stride + (int64_t)g * D) * ES;
+      vec = *reinterpret_cast<const u32x4*>(src + c * 16);
+    }
+  }
+
+  __device__ inline void stage(char* stage) const {
+    const int t = threadIdx.x;
+    if (t >= 2 * NC) return;
+    const bool is_v = t >= NC;
+    const int c = is_v ? t - NC : t;
+    *reinterpret_cast<u32x4*>(stage + (is_v ? D * ES : 0) + c * 16) = vec;
+  }
+
+  __device__ inline void store(const DecodeArgs& a, const int32_t* trow, int j, int g,
+                               int o) const {
+    constexpr int64_t kTile = (int64_t)kBlock * D * ES;
+    const int t = threadIdx.x;
+    if (t >= 2 * NC) return;
+    const int phys = trow[j];
+    if (phys < 0 || phys >= a.num_blocks) return;
+    const bool is_v = t >= NC;
+    const int c = is_v ? t - NC : t;
+    char* tile = (is_v ? a.v_pool : a.k_pool) + ((int64_t)phys * a.num_kv_heads + g) * kTile;
+    if (!is_v) {
+      *reinterpret_cast<u32x4*>(tile + ((int64_t)o * D + c * X) * ES) = vec;
+    } else {
+      char* vb = tile + ((int64_t)(o >> 2) * D * 4 + (o & 3)) * ES;
+#pragma unroll
+      for (int e = 0; e < X; ++e) {
+        const int d = c * X + e;
+        if constexpr (ES == 4)
+          *reinterpret_cast<uint32_t*>(vb + (int64_t)d * 4 * ES) = vec[e];
+        else
+          *reinterpret_cast<uint16_t*>(vb + (int64_t)d * 4 * ES) =
+              (uint16_t)(vec[e >> 1] >> ((e & 1) * 16));
+      }
+    }
+  }
+
 };
 
 // Running softmax state of one wavefront: lane (h + 16 q) owns head h;
@@ -306,8 +419,15 @@ template <> struct Elt<TagF32> { using T = float; static constexpr int bytes = 4
 #define PA_WAVES_PER_EU 3
 #endif
 
+// Occupancy target: 3 wavefronts per SIMD (<= 168 VGPRs) keeps a block in
+// flight per wavefront on top of the one being computed; fp32 tiles of 128
+// dims need twice the fragment registers, so they run at 2.
+template <class Tag, int D> struct WavesPerEU {
+  static constexpr int value = (!Is16<Tag>::value && D == 128) ? 2 : PA_WAVES_PER_EU;
+};
+
 template <class Tag, int D, class OutT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   constexpr int ES = Elt<Tag>::bytes;
@@ -363,40 +483,70 @@ void decode_kernel(DecodeArgs a) {
   const int64_t head_tile = (int64_t)g * kTileBytes;
   const int64_t block_stride = (int64_t)a.num_kv_heads * kTileBytes;
 
-  for (int c0 = 0; c0 < cnt; c0 += kWave) {
-    const int n = min(kWave, cnt - c0);
-    const int tb = lane < n ? trow[first + kWaves * (c0 + lane)] : 0;
-    // Block i of this chunk: physical id (0 when out of range: loads stay in
-    // bounds and the block contributes nothing) and its valid-token count.
-    auto phys_of = [&](int i, int& nv) {
-      int phys = __builtin_amdgcn_readlane(tb, i);
-      const int j = first + kWaves * (c0 + i);
-      nv = min(kBlock, L - j * kBlock);
-      if (phys < 0 || phys >= a.num_blocks) { phys = 0; nv = 0; }
-      return phys;
-    };
-    // Two register buffers, one block ahead.  The steady-state loop has no
-    // conditional loads, so each computation waits only for its own block.
-    Frag<Tag, D> fa, fb;
-    int nva, nvb;
-    auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
-      const int64_t off = (int64_t)phys_of(i, nv) * block_stride + head_tile;
-      f.load(a.k_pool + off, a.v_pool + off, lane);
-    };
-    // Loads are unconditional so that every computation waits only for its own
-    // block (a conditional load makes the wait counts path-dependent and the
-    // compiler falls back to waiting for everything).  Past the last block the
-    // index is clamped: the spare load re-reads a block the wavefront just
-    // fetched.
+  // Fused step: the unit holding position L-1 writes the current token.
+  const int j_new = (L - 1) / kBlock;
+  const int o_new = (L - 1) % kBlock;
+  const bool own_new = a.k_new != nullptr && j_new >= j0 && j_new < j1;
+  char* stage = reinterpret_cast<char*>(smem) + a.stage_off;
+  NewToken<Tag, D> tok;
+  if (own_new) tok.load(a, seq, g);             // in flight with the first blocks
+
+  // Blocks are processed in chunks of up to 64 per wavefront: one table load
+  // per chunk, each id broadcast with readlane.
+  Frag<Tag, D> fa, fb;
+  int nva = 0, nvb = 0;
+  int c0 = 0, n = 0, tb = 0;
+  // Block i of the chunk: physical id (0 when out of range: loads stay in
+  // bounds and the block contributes nothing) and its valid-token count,
+  // negated for the block that holds the current token (patched first).
+  auto phys_of = [&](int i, int& nv) {
+    int phys = __builtin_amdgcn_readlane(tb, i);
+    const int j = first + kWaves * (c0 + i);
+    nv = min(kBlock, L - j * kBlock);
+    if (phys < 0 || phys >= a.num_blocks) { phys = 0; nv = 0; }
+    if (own_new && j == j_new) nv = -nv;
+    return phys;
+  };
+  auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
+    const int64_t off = (int64_t)phys_of(i, nv) * block_stride + head_tile;
+    f.load(a.k_pool + off, a.v_pool + off, lane);
+  };
+  auto attend = [&](Frag<Tag, D>& f, int nv) {
+    if (nv < 0) {
+      patch_token<Tag, D>(f, stage, o_new, lane);
+      nv = -nv;
+    }
+    if (nv > 0) attend_block<Tag, D>(f, qf, st, nv, a.qk_scale, lane);
+  };
+  auto open_chunk = [&]() {
+    n = min(kWave, cnt - c0);
+    tb = lane < n ? trow[first + kWaves * (c0 + lane)] : 0;
     load_into(fa, 0, nva);
+  };
+
+  if (cnt > 0) open_chunk();
+  if (own_new) {                                // every wavefront reaches this barrier
+    tok.stage(stage);
+    __syncthreads();
+  }
+  // Two register buffers, one block ahead.  Loads are unconditional so that
+  // every computation waits only for its own block (a conditional load makes
+  // the wait counts path-dependent and the compiler falls back to waiting
+  // for everything); past the last block the index is clamped and the spare
+  // load re-reads a block the wavefront just fetched.
+  for (; c0 < cnt; c0 += kWave) {
+    if (c0 > 0) open_chunk();
     for (int i = 0; i < n; i += 2) {
       load_into(fb, min(i + 1, n - 1), nvb);
-      if (nva > 0) attend_block<Tag, D>(fa, qf, st, nva, a.qk_scale, lane);
+      attend(fa, nva);
       if (i + 1 >= n) break;
       load_into(fa, min(i + 2, n - 1), nva);
-      if (nvb > 0) attend_block<Tag, D>(fb, qf, st, nvb, a.qk_scale, lane);
+      attend(fb, nvb);
     }
   }
+  // Pool write of the current token after the loop: a store while the same
+  // tile streams in makes those loads wait on it.
+  if (own_new) tok.store(a, trow, j_new, g, o_new);
 
   // ---- merge the four wavefronts (LDS) ----
   const float l_tot = xor_sum(st.l);
@@ -515,6 +665,97 @@ static size_t workspace_bytes(int64_t rows, int32_t parts, int32_t D) {
   return (size_t)(2 * ml_pad + rows * parts * (int64_t)D * 4);
 }
 
+
+// Shared by pa_decode_attention (k_new == null) and pa_decode_step.
+static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                             const void* k_new, const void* v_new, int64_t new_stride,
+                             const void* q, void* out, pa_dtype out_dtype,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             float scale, int32_t max_context_len, int32_t partition_size,
+                             void* workspace, size_t workspace_size, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  if (G > 16) return PA_ERR_UNSUPPORTED;
+  if (partition_size % kBlock) return PA_ERR_INVALID_ARG;
+  if (out_dtype != PA_F32 && out_dtype != pool->dtype) return PA_ERR_UNSUPPORTED;
+  const int es = elem_bytes(pool->dtype);
+  if (k_new) {
+    if (new_stride < (int64_t)pool->num_kv_heads * pool->head_dim || (new_stride * es) % 16 ||
+        !aligned16(k_new) || !aligned16(v_new))
+      return PA_ERR_INVALID_ARG;
+  }
+  if (num_seqs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !out || !context_lens) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(q)) return PA_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PA_ERR_INVALID_ARG;
+
+  int32_t ps, parts;
+  geometry(max_context_len, partition_size, &ps, &parts);
+  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  const size_t need = workspace_bytes(rows, parts, pool->head_dim);
+  if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+  const int64_t units = (int64_t)pool->num_kv_heads * num_seqs * parts;
+  if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
+
+  DecodeArgs a;
+  a.k_pool = (char*)k_pool;
+  a.v_pool = (char*)v_pool;
+  a.k_new = (const char*)k_new;
+  a.v_new = (const char*)v_new;
+  a.new_stride = new_stride;
+  a.q = (const char*)q;
+  a.out = out;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.part_m = a.part_l = a.part_o = nullptr;
+  if (need > 0) {
+    const int64_t ml = rows * parts * 4;
+    const int64_t ml_pad = (ml + 255) / 256 * 256;
+    a.part_m = (float*)workspace;
+    a.part_l = (float*)((char*)workspace + ml_pad);
+    a.part_o = (float*)((char*)workspace + 2 * ml_pad);
+  }
+  a.num_blocks = pool->num_blocks;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = G;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_len = max_context_len;
+  a.ps = ps;
+  a.num_parts = parts;
+  a.longest_first = num_seqs <= kRankMax ? 1 : 0;
+  a.qk_scale = scale * kLog2e;
+  // LDS: [merge area | staged current token]; the ranking keys alias the start.
+  const size_t merge = ((size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float) + 15) / 16 * 16;
+  a.stage_off = (int32_t)merge;
+  size_t lds = merge + (k_new ? (size_t)2 * pool->head_dim * es : 0);
+  if (a.longest_first) lds = std::max(lds, (size_t)(kRankMax + 1) * sizeof(uint32_t));
+  const hipStream_t s = (hipStream_t)stream;
+  const int D = pool->head_dim;
+
+  switch (pool->dtype) {
+    case PA_BF16:
+      return out_dtype == PA_F32 ? dispatch_d<TagBF16, float>(D, a, units, lds, s)
+                                 : dispatch_d<TagBF16, __bf16>(D, a, units, lds, s);
+    case PA_F16:
+      return out_dtype == PA_F32 ? dispatch_d<TagF16, float>(D, a, units, lds, s)
+                                 : dispatch_d<TagF16, _Float16>(D, a, units, lds, s);
+    case PA_F32:
+      return dispatch_d<TagF32, float>(D, a, units, lds, s);
+    default:
+      return PA_ERR_UNSUPPORTED;
+  }
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -542,74 +783,22 @@ pa_status pa_decode_attention(const pa_pool_desc* pool, const void* k_pool, cons
                               int32_t num_q_heads, float scale, int32_t max_context_len,
                               int32_t partition_size, void* workspace, size_t workspace_size,
                               void* stream) {
-  pa_status st = check_pool(pool);
-  if (st != PA_OK) return st;
-  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0 || max_context_len < 0 ||
-      partition_size < 0)
-    return PA_ERR_INVALID_ARG;
-  if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
-  const int32_t G = num_q_heads / pool->num_kv_heads;
-  if (G > 16) return PA_ERR_UNSUPPORTED;
-  if (partition_size % kBlock) return PA_ERR_INVALID_ARG;
-  if (out_dtype != PA_F32 && out_dtype != pool->dtype) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (!k_pool || !v_pool || !q || !out || !context_lens) return PA_ERR_INVALID_ARG;
-  if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
-  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(q)) return PA_ERR_INVALID_ARG;
-  if (!(scale == scale)) return PA_ERR_INVALID_ARG;
+  return decode_impl(pool, (void*)k_pool, (void*)v_pool, nullptr, nullptr, 0, q, out, out_dtype,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                     scale, max_context_len, partition_size, workspace, workspace_size, stream);
+}
 
-  int32_t ps, parts;
-  geometry(max_context_len, partition_size, &ps, &parts);
-  const int64_t rows = (int64_t)num_seqs * num_q_heads;
-  const size_t need = workspace_bytes(rows, parts, pool->head_dim);
-  if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
-    return PA_ERR_WORKSPACE;
-  const int64_t units = (int64_t)pool->num_kv_heads * num_seqs * parts;
-  if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
-
-  DecodeArgs a;
-  a.k_pool = (const char*)k_pool;
-  a.v_pool = (const char*)v_pool;
-  a.q = (const char*)q;
-  a.out = out;
-  a.tables = block_tables;
-  a.lens = context_lens;
-  a.part_m = a.part_l = a.part_o = nullptr;
-  if (need > 0) {
-    const int64_t ml = rows * parts * 4;
-    const int64_t ml_pad = (ml + 255) / 256 * 256;
-    a.part_m = (float*)workspace;
-    a.part_l = (float*)((char*)workspace + ml_pad);
-    a.part_o = (float*)((char*)workspace + 2 * ml_pad);
-  }
-  a.num_blocks = pool->num_blocks;
-  a.num_kv_heads = pool->num_kv_heads;
-  a.num_q_heads = num_q_heads;
-  a.group = G;
-  a.num_seqs = num_seqs;
-  a.max_blocks = max_blocks_per_seq;
-  a.max_len = max_context_len;
-  a.ps = ps;
-  a.num_parts = parts;
-  a.longest_first = num_seqs <= kRankMax ? 1 : 0;
-  a.qk_scale = scale * kLog2e;
-  size_t lds = (size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float);
-  if (a.longest_first) lds = std::max(lds, (size_t)(kRankMax + 1) * sizeof(uint32_t));
-  const hipStream_t s = (hipStream_t)stream;
-  const int D = pool->head_dim;
-
-  switch (pool->dtype) {
-    case PA_BF16:
-      return out_dtype == PA_F32 ? dispatch_d<TagBF16, float>(D, a, units, lds, s)
-                                 : dispatch_d<TagBF16, __bf16>(D, a, units, lds, s);
-    case PA_F16:
-      return out_dtype == PA_F32 ? dispatch_d<TagF16, float>(D, a, units, lds, s)
-                                 : dispatch_d<TagF16, _Float16>(D, a, units, lds, s);
-    case PA_F32:
-      return dispatch_d<TagF32, float>(D, a, units, lds, s);
-    default:
-      return PA_ERR_UNSUPPORTED;
-  }
+pa_status pa_decode_step(const pa_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
+                         const void* v_new, int64_t new_stride, const void* q, void* out,
+                         pa_dtype out_dtype, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, float scale,
+                         int32_t max_context_len, int32_t partition_size, void* workspace,
+                         size_t workspace_size, void* stream) {
+  if (!k_new || !v_new) return PA_ERR_INVALID_ARG;
+  return decode_impl(pool, k_pool, v_pool, k_new, v_new, new_stride, q, out, out_dtype,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                     scale, max_context_len, partition_size, workspace, workspace_size, stream);
 }
 
 }  // extern "C"

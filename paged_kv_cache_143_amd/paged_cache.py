@@ -174,11 +174,14 @@ def build_batch(w: Workload, device: str = "cuda", poison: bool = True,
 
 
 class DecodeStep:
-    """One decode iteration over a batch: slot mapping + write of every sequence's
-    current token (position L - 1), then decode attention."""
+    """One decode iteration over a batch: write every sequence's current token
+    (position L - 1) and attend.  fused=True issues pa_decode_step (one launch);
+    fused=False issues pa_slot_mapping, pa_write_kv and pa_decode_attention."""
 
-    def __init__(self, batch: Batch, partition_size: int = 0, out_dtype=torch.float32):
+    def __init__(self, batch: Batch, partition_size: int = 0, out_dtype=torch.float32,
+                 fused: bool = True):
         self.b = batch
+        self.fused = fused
         w = batch.w
         dev = batch.q.device
         S = w.num_seqs
@@ -202,7 +205,16 @@ class DecodeStep:
         B.decode_attention_t(b.kv.desc, b.kv.k, b.kv.v, b.q, self.out, b.tables, b.lens,
                              b.w.scale, b.max_len, self.partition_size, self.workspace)
 
+    def fused_step(self) -> None:
+        b = self.b
+        B.decode_step_t(b.kv.desc, b.kv.k, b.kv.v, self.k_new, self.v_new, b.q, self.out,
+                        b.tables, b.lens, b.w.scale, b.max_len, self.partition_size,
+                        self.workspace)
+
     def __call__(self) -> torch.Tensor:
-        self.write_current()
-        self.attend()
+        if self.fused:
+            self.fused_step()
+        else:
+            self.write_current()
+            self.attend()
         return self.out

@@ -38,13 +38,11 @@ def require_gpu():
 
 def pool_logical(kv, num_kv_heads: int, head_dim: int):
     """Device pools -> fp64 CPU arrays [blocks][offset][head][dim], read through the
-    pool layout of include/pa.h (K: [d/X][b][X] tiles, V: [d][b] tiles)."""
-    es = kv.k.element_size()
-    X = 16 // es
+    pool layout of include/pa.h (K tiles [b][d]; V tiles [b/4][d][4])."""
     nb = kv.k.numel() // (num_kv_heads * BLOCK * head_dim)
-    k = kv.k.view(nb, num_kv_heads, head_dim // X, BLOCK, X).permute(0, 3, 1, 2, 4)
-    k = k.reshape(nb, BLOCK, num_kv_heads, head_dim)
-    v = kv.v.view(nb, num_kv_heads, head_dim, BLOCK).permute(0, 3, 1, 2)
+    k = kv.k.view(nb, num_kv_heads, BLOCK, head_dim).permute(0, 2, 1, 3)
+    v = kv.v.view(nb, num_kv_heads, BLOCK // 4, head_dim, 4).permute(0, 2, 4, 1, 3)
+    v = v.reshape(nb, BLOCK, num_kv_heads, head_dim)
     return (k.to(torch.float64).cpu().numpy(), v.to(torch.float64).cpu().numpy())
 
 

@@ -102,6 +102,25 @@ def test_decode_argument_checks():
     assert call(max_context_len=-1) == B.PA_ERR_INVALID_ARG
 
 
+def test_decode_step_argument_checks():
+    d = _desc()
+    base = dict(k_pool=16, v_pool=16, k_new=16, v_new=16, new_stride=1024, q=16, out=16,
+                out_dtype=B.PA_F32, block_tables=16, max_blocks_per_seq=4, context_lens=16,
+                num_seqs=2, num_q_heads=32, scale=0.1, max_context_len=64, partition_size=0,
+                workspace=0, workspace_bytes=0, stream=0)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return B.pa_decode_step(d, **a)
+
+    assert call(k_new=0) == B.PA_ERR_INVALID_ARG
+    assert call(new_stride=1000) == B.PA_ERR_INVALID_ARG          # shorter than a row
+    assert call(new_stride=1028) == B.PA_ERR_INVALID_ARG          # not 16-byte multiple
+    assert call(v_new=24) == B.PA_ERR_INVALID_ARG                 # misaligned
+    assert call(num_seqs=0) == B.PA_OK
+
+
 def test_validate_argument_checks():
     d = _desc()
     assert B.pa_validate_tables(d, 16, 4, 16, 2, 64, 0, 0) == B.PA_ERR_INVALID_ARG

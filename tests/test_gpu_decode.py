@@ -179,3 +179,58 @@ def test_gqa_batch256_full_size_sampled(ps):
     err = row_rel_err(got, ref)
     announce(f"gqa-bf16-b256 ps={ps}: rows {rows} max row rel err {err:.3e}")
     assert err <= 2e-3
+
+
+def _poison_current_tokens(batch):
+    """Overwrite every sequence's current token (position L-1) in the pool with NaN."""
+    w = batch.w
+    slots = [batch.bm.slot(n, batch.bm.lengths[n] - 1) for n in w.seq_names]
+    shape = (len(slots), w.num_kv_heads, w.head_dim)
+    nan = torch.full(shape, float("nan"), dtype=W.DTYPES[w.dtype], device="cuda")
+    batch.kv.write(nan, nan, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+
+
+FUSED = {
+    "tiny-f32": (W.tiny_f32, 0),
+    "gqa4-bf16-d128": (lambda: W.scaled("fg4", 71, 9, 1, 700, 32, 8, 128, "bf16"), 0),
+    "gqa2-f16-d64-split": (lambda: W.scaled("fg2", 72, 6, 1, 500, 4, 2, 64, "f16"), 32),
+    "gqa3-f32-d128-split": (lambda: W.scaled("fg3", 73, 4, 1, 300, 6, 2, 128, "f32"), 64),
+    "cow-bf16": (lambda: W.shared_prefix("fcow", 74, "bf16", 2, 8, 1016, 1, 40, 8, 2, 64, 200), 0),
+    "edges-bf16": (lambda: W.independent("fedge", 75, "bf16", [1, 15, 16, 17, 31, 32, 33, 2],
+                                          8, 2, 128, 40), 0),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_step_equals_three_calls_and_oracle(name):
+    make, ps = FUSED[name]
+    w = make()
+    outs, pools = [], []
+    for fused in (False, True):
+        batch = build_batch(w, drop_payload_cache=False)
+        _poison_current_tokens(batch)
+        step = DecodeStep(batch, partition_size=ps, fused=fused)
+        outs.append(step().clone())
+        torch.cuda.synchronize()
+        pools.append((batch.kv.k.clone(), batch.kv.v.clone()))
+    assert torch.equal(outs[0], outs[1])
+    bits = lambda t: t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+    for a, b in zip(pools[0], pools[1]):
+        assert torch.equal(bits(a), bits(b))
+    ref = OracleRun(w).decode()
+    err = row_rel_err(outs[1].cpu().numpy().astype(np.float64), ref)
+    announce(f"fused {name}: max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
+
+
+def test_fused_step_full_size_sampled():
+    """The batch-256 GQA workload in the benchmark's launch configuration."""
+    w = W.gqa_bf16()
+    batch = build_batch(w, drop_payload_cache=False)
+    _poison_current_tokens(batch)
+    out = DecodeStep(batch, partition_size=0, fused=True)().cpu().numpy().astype(np.float64)
+    rows = [0, 3, 64, 127, 128, 191, 250, 255]
+    ref = OracleRun(w).decode(rows=rows)
+    err = row_rel_err(out[rows], ref)
+    announce(f"fused gqa-bf16-b256: max row rel err {err:.3e}")
+    assert err <= 2e-3

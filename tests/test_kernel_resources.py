@@ -1,0 +1,41 @@
+"""Compile the HIP sources to gfx950 assembly (no GPU needed) and check each
+kernel's resource metadata: no scratch (private) memory -- a register array
+indexed at run time silently moves to scratch and costs 2x in bandwidth -- and
+decode kernels within the VGPR budget of their occupancy target."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_143_amd import build as B
+
+SRC = os.path.join(B.CSRC, "pa_decode.hip")
+
+
+def _kernels(path, tmp_path):
+    out = str(tmp_path / "k.s")
+    cmd = [B.hipcc(), "-O3", "-std=c++17", f"--offload-arch={B.ARCH}", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", f"-I{B.INCLUDE}", f"-I{B.CSRC}", "--offload-device-only",
+           "-S", path, "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = open(out).read()
+    ks = {}
+    for blk in text.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", blk).group(1)
+        ks[name] = (int(re.search(r"\.vgpr_count:\s+(\d+)", blk).group(1)),
+                    int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", blk).group(1)))
+    return ks, text
+
+
+@pytest.mark.parametrize("src", ["pa_decode.hip", "pa_cache.hip"])
+def test_no_scratch_and_vgpr_budget(src, tmp_path):
+    ks, text = _kernels(os.path.join(B.CSRC, src), tmp_path)
+    assert ks
+    for name, (vgpr, scratch) in ks.items():
+        assert scratch == 0, f"{name} uses {scratch} bytes of scratch"
+        if "decode_kernel" in name:
+            budget = 256 if ("TagF32ELi128" in name) else 168      # 2 or 3 waves per SIMD
+            assert vgpr <= budget, f"{name}: {vgpr} VGPRs"
+    # no writes through the scalar data cache anywhere
+    assert not re.search(r"^\s*s_(store|atomic|dcache_wb|buffer_store)", text, re.M)
