@@ -100,6 +100,15 @@ def run(args):
         sys.exit("bench.py needs a GPU")
     binding.lib()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # A plain copy of known size (read 512 MiB + write 512 MiB per launch):
+        # hardware byte counters read on it give their scale to true bytes.
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = W.gqa_bf16()
     t_setup = time.perf_counter()
     batch = build_batch(w, device="cuda")
@@ -116,24 +125,31 @@ def run(args):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        # One event per boundary: before every launch and after the last, so
+        # the markers add as little as possible between kernels.
+        mk = lambda: torch.cuda.Event(enable_timing=True)
+        ev_kv = [mk() for _ in range(args.steps)]          # before each KV-reading launch
+        ev_w = [mk() for _ in range(args.steps)] if args.unfused else None
+        ev_end = mk()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for e0, e1, e2 in ev:
-            e0.record()
-            if not args.unfused:
-                e1.record()
-                step.fused_step()
-            else:
+        for k in range(args.steps):
+            if args.unfused:
+                ev_w[k].record()
                 step.write_current()
-                e1.record()
+                ev_kv[k].record()
                 step.attend()
-            e2.record()
+            else:
+                ev_kv[k].record()
+                step.fused_step()
+        ev_end.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        write_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
-        dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+        nxt = [(ev_w[k + 1] if args.unfused else ev_kv[k + 1]) if k + 1 < args.steps else ev_end
+               for k in range(args.steps)]
+        dec_ms = np.array([ev_kv[k].elapsed_time(nxt[k]) for k in range(args.steps)])
+        write_ms = (np.array([ev_w[k].elapsed_time(ev_kv[k]) for k in range(args.steps)])
+                    if args.unfused else np.zeros(args.steps))
         results[ps] = (wall / args.steps * 1e3, write_ms, dec_ms)
         print(f"[bench] partition {ps}{' unfused' if args.unfused else ''}: step "
               f"{wall / args.steps * 1e3:.4f} ms, KV-reading launch median "
@@ -201,6 +217,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="three launches per step instead of pa_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run three plain 512 MiB device copies (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work in the CPU baseline sample")
     args = ap.parse_args()

@@ -162,13 +162,28 @@ __device__ inline float xor_sum(float v) {
 // (8 bytes; each instruction reads four full 128-byte lines).
 template <class Tag, int D, bool H = Is16<Tag>::value> struct Frag;
 
-// KV tiles are read exactly once per call: streaming (non-temporal) loads.
-template <class T> __device__ inline T stream_load(const char* p) {
+// KV tiles are read exactly once per call: streaming (non-temporal) buffer
+// loads.  Each tile gets its own buffer resource (base = tile address, size =
+// tile bytes); a resource of size 0 makes every lane's access out of range,
+// which returns zeros without touching memory -- the one-block-ahead prefetch
+// uses that past a wavefront's last block, so its wait counts stay static
+// without a spare read of real data.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;         // raw (untyped) buffer, gfx9 family
 #if PA_TEMPORAL_KV
-  return *reinterpret_cast<const T*>(p);
+constexpr int kKvCachePolicy = 0;
 #else
-  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+constexpr int kKvCachePolicy = 2;              // nt
 #endif
+
+__device__ inline rsrc_t tile_rsrc(const char* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), 0, bytes, kRsrcWord3);
+}
+__device__ inline u32x4 buf_load16(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kKvCachePolicy);
+}
+__device__ inline u32x2 buf_load8(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kKvCachePolicy);
 }
 
 template <class Tag, int D> struct Frag<Tag, D, true> {
@@ -176,13 +191,13 @@ template <class Tag, int D> struct Frag<Tag, D, true> {
   static constexpr int NV = D / 16;
   u32x4 k[NK];
   u32x2 v[NV];
-  __device__ inline void load(const char* kt, const char* vt, int lane) {
-    const char* kr = kt + (lane & 15) * (D * 2) + (lane >> 4) * 16;
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
+    const int kr = (lane & 15) * (D * 2) + (lane >> 4) * 16;
 #pragma unroll
-    for (int m = 0; m < NK; ++m) k[m] = stream_load<u32x4>(kr + m * 64);
-    const char* vr = vt + (lane >> 4) * (D * 8) + (lane & 15) * 8;
+    for (int m = 0; m < NK; ++m) k[m] = buf_load16(rk, kr + m * 64);
+    const int vr = (lane >> 4) * (D * 8) + (lane & 15) * 8;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) v[n] = stream_load<u32x2>(vr + n * 128);
+    for (int n = 0; n < NV; ++n) v[n] = buf_load8(rv, vr + n * 128);
   }
 };
 
@@ -194,13 +209,13 @@ template <class Tag, int D> struct Frag<Tag, D, false> {
   static constexpr int NV = D / 16;
   f32x4 k[NK];
   f32x4 v[NV];
-  __device__ inline void load(const char* kt, const char* vt, int lane) {
-    const char* kr = kt + (lane & 15) * (D * 4) + (lane >> 4) * 16;
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
+    const int kr = (lane & 15) * (D * 4) + (lane >> 4) * 16;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) k[j] = stream_load<f32x4>(kr + j * 64);
-    const char* vr = vt + (lane >> 4) * (D * 16) + (lane & 15) * 16;
+    for (int j = 0; j < NK; ++j) k[j] = __builtin_bit_cast(f32x4, buf_load16(rk, kr + j * 64));
+    const int vr = (lane >> 4) * (D * 16) + (lane & 15) * 16;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) v[n] = stream_load<f32x4>(vr + n * 256);
+    for (int n = 0; n < NV; ++n) v[n] = __builtin_bit_cast(f32x4, buf_load16(rv, vr + n * 256));
   }
 };
 
@@ -499,17 +514,18 @@ void decode_kernel(DecodeArgs a) {
   // Block i of the chunk: physical id (0 when out of range: loads stay in
   // bounds and the block contributes nothing) and its valid-token count,
   // negated for the block that holds the current token (patched first).
-  auto phys_of = [&](int i, int& nv) {
-    int phys = __builtin_amdgcn_readlane(tb, i);
-    const int j = first + kWaves * (c0 + i);
-    nv = min(kBlock, L - j * kBlock);
-    if (phys < 0 || phys >= a.num_blocks) { phys = 0; nv = 0; }
-    if (own_new && j == j_new) nv = -nv;
-    return phys;
-  };
+  // i == n is the prefetch past the wavefront's last block: a size-0
+  // resource, like a table entry outside the pool.
   auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
-    const int64_t off = (int64_t)phys_of(i, nv) * block_stride + head_tile;
-    f.load(a.k_pool + off, a.v_pool + off, lane);
+    int phys = __builtin_amdgcn_readlane(tb, min(i, n - 1));
+    const int j = first + kWaves * (c0 + i);
+    const bool ok = i < n && phys >= 0 && phys < a.num_blocks;
+    nv = ok ? min(kBlock, L - j * kBlock) : 0;
+    if (!ok) phys = 0;
+    if (own_new && j == j_new) nv = -nv;
+    const int64_t off = (int64_t)phys * block_stride + head_tile;
+    const int bytes = ok ? (int)kTileBytes : 0;
+    f.load(tile_rsrc(a.k_pool + off, bytes), tile_rsrc(a.v_pool + off, bytes), lane);
   };
   auto attend = [&](Frag<Tag, D>& f, int nv) {
     if (nv < 0) {
@@ -532,15 +548,14 @@ void decode_kernel(DecodeArgs a) {
   // Two register buffers, one block ahead.  Loads are unconditional so that
   // every computation waits only for its own block (a conditional load makes
   // the wait counts path-dependent and the compiler falls back to waiting
-  // for everything); past the last block the index is clamped and the spare
-  // load re-reads a block the wavefront just fetched.
+  // for everything); past the last block the load is an empty-resource one.
   for (; c0 < cnt; c0 += kWave) {
     if (c0 > 0) open_chunk();
     for (int i = 0; i < n; i += 2) {
-      load_into(fb, min(i + 1, n - 1), nvb);
+      load_into(fb, i + 1, nvb);
       attend(fa, nva);
       if (i + 1 >= n) break;
-      load_into(fa, min(i + 2, n - 1), nva);
+      load_into(fa, i + 2, nva);
       attend(fb, nvb);
     }
   }
