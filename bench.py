@@ -33,6 +33,27 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 DEFAULT_PARTITION = 0
+COUNTERS = os.path.join(ROOT, "profiles", "decode_step_gqa_bf16_b256_counters.json")
+KERNEL_SOURCES = ("paged_kv_cache_143_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_143_amd/csrc/pa_internal.h")
+
+
+def _measured_traffic(fused: bool, partition: int):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record, only while the kernel sources are the ones it was taken on (and for
+    the configuration it was taken in); otherwise None."""
+    import hashlib
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("kernel_source_sha256") != h.hexdigest() or not fused or partition != 0:
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def _algorithmic_bytes(w, lens, fused):
@@ -192,7 +213,7 @@ def run(args):
                        "kv_launch_mean": round(dec_mean_s * 1e6, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": _measured_traffic(not args.unfused, ps),
                      "kernel": ("pa_decode_attention" if args.unfused else "pa_decode_step")
                      + " (decode_kernel" + (" + reduce_kernel" if ps and ps < int(lens.max())
                                             else "") + ")",
