@@ -38,6 +38,21 @@ KERNEL_SOURCES = ("paged_kv_cache_143_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_143_amd/csrc/pa_internal.h")
 
 
+# name -> (constructor, default partition size, length description, headline?)
+def _workloads():
+    from paged_kv_cache_143_amd import workloads as W
+    return {
+        "gqa-bf16-b256": (W.gqa_bf16, 0, "uniform int 200..2000"),
+        "opt13b-mha-f16": (W.opt13b_f16, 0, "uniform int 200..2000"),
+        "shared-prefix-bf16-p1024": (lambda: W.shared_prefix_bf16(prompt_len=1024), 0,
+                                     "1024-token prompt + tails uniform 1..512"),
+        "shared-prefix-bf16-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
+                                     "1016-token prompt + tails uniform 1..512"),
+        "long-ctx-splitk-bf16": (W.long_ctx_bf16, 512, "uniform int 8192..32768"),
+        "tiny-f32": (W.tiny_f32, 0, "{50, 20, 65, 16}"),
+    }
+
+
 def _measured_traffic(fused: bool, partition: int):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record, only while the kernel sources are the ones it was taken on (and for
@@ -98,7 +113,7 @@ def cpu_baseline(w, budget_s: float):
             paged_decode(pool, resolve, tables, lens, q64, w.num_kv_heads, w.scale, rows=[i])
             elapsed += time.perf_counter() - t0
             w.drop_cache()
-            kv_bytes += lens[i] * w.num_kv_heads * w.head_dim * 2 * 2
+            kv_bytes += lens[i] * w.num_kv_heads * w.head_dim * 2 * (4 if w.dtype == "f32" else 2)
             tokens += lens[i]
             done += 1
             if elapsed >= budget_s:
@@ -130,7 +145,10 @@ def run(args):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    w = W.gqa_bf16()
+    make, default_ps, length_desc = _workloads()[args.workload]
+    w = make()
+    if args.partition is None:
+        args.partition = default_ps
     t_setup = time.perf_counter()
     batch = build_batch(w, device="cuda")
     lens = batch.bm.length_array(w.seq_names)
@@ -194,10 +212,10 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "gqa-bf16-b256", "num_seqs": w.num_seqs,
-                   "lengths": "uniform int 200..2000", "context_tokens": int(lens.sum()),
+        "config": {"workload": args.workload, "num_seqs": w.num_seqs,
+                   "lengths": length_desc, "context_tokens": int(lens.sum()),
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "partition_size": ps, "out_dtype": "f32", "seed": w.seed,
@@ -213,7 +231,8 @@ def run(args):
                        "kv_launch_mean": round(dec_mean_s * 1e6, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _measured_traffic(not args.unfused, ps),
+                     "traffic": (_measured_traffic(not args.unfused, ps)
+                                 if args.workload == "gqa-bf16-b256" else None),
                      "kernel": ("pa_decode_attention" if args.unfused else "pa_decode_step")
                      + " (decode_kernel" + (" + reduce_kernel" if ps and ps < int(lens.max())
                                             else "") + ")",
@@ -222,7 +241,7 @@ def run(args):
     if args.sweep:
         line["sweep_ms_per_step"] = {str(p): round(v[0], 5) for p, v in results.items()}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(W.gqa_bf16(), args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(make(), args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 
@@ -231,8 +250,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--partition", type=int, default=DEFAULT_PARTITION,
-                    help="partition size in tokens (0 = one work unit per sequence and KV head)")
+    ap.add_argument("--workload", default="gqa-bf16-b256", choices=sorted(_workloads()),
+                    help="the headline metric is quoted on gqa-bf16-b256 (the default)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="partition size in tokens (0 = one work unit per sequence and KV head; "
+                         "default: 0, or 512 for the long-context workload)")
     ap.add_argument("--sweep", type=int, nargs="*", default=None,
                     help="time several partition sizes and report the fastest")
     ap.add_argument("--unfused", action="store_true",

@@ -234,3 +234,31 @@ def test_fused_step_full_size_sampled():
     err = row_rel_err(out[rows], ref)
     announce(f"fused gqa-bf16-b256: max row rel err {err:.3e}")
     assert err <= 2e-3
+
+
+FULL = {
+    "opt13b-mha-f16": (W.opt13b_f16, 0, [0, 17, 40, 63], None),
+    "shared-prefix-p1024": (lambda: W.shared_prefix_bf16(prompt_len=1024), 0,
+                            [0, 7, 8, 100, 255], 0),
+    "shared-prefix-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
+                            [0, 1, 7, 8, 130, 255], 32 * 7),
+    "long-ctx-splitk": (W.long_ctx_bf16, 512, [0, 5, 15], None),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_workloads_sampled(name):
+    """The other workloads at full size, in the benchmark's step (pa_decode_step with
+    the current tokens first poisoned in the pool), sampled rows vs the oracle."""
+    make, ps, rows, copies = FULL[name]
+    w = make()
+    batch = build_batch(w, drop_payload_cache=False)
+    if copies is not None:
+        assert len(batch.copies) == copies
+    _poison_current_tokens(batch)
+    out = DecodeStep(batch, partition_size=ps, fused=True)().cpu().numpy().astype(np.float64)
+    ref = OracleRun(w).decode(rows=rows)
+    err = row_rel_err(out[rows], ref)
+    announce(f"{name} ps={ps}: rows {rows} max row rel err {err:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= tol_for(w.dtype)
