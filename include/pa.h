@@ -156,7 +156,9 @@ PA_API pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode_attention
  * needs for these arguments (0 when partition_size == 0 or when every
- * sequence fits in one partition).  `bytes` is host memory.
+ * sequence fits in one partition): one fp32 record per (sequence, KV head,
+ * partition) of G*head_dim + 2*G floats rounded up to 128 bytes, G = Hq/Hkv.
+ * `bytes` is host memory; num_q_heads must be a multiple of num_kv_heads.
  */
 PA_API pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
                                    int32_t num_q_heads, int32_t max_context_len,

@@ -70,9 +70,9 @@ struct DecodeArgs {
   void* out;
   const int32_t* tables;
   const int32_t* lens;
-  float* part_m;       // [S][Hq][P]
-  float* part_l;       // [S][Hq][P]
-  float* part_o;       // [S][Hq][P][D]
+  float* part;         // split partials: one record per (seq, KV head, partition):
+                       // o/l [G][D], then m [G], then l [G], padded to 128 bytes
+  int32_t part_stride; // floats per record
   int32_t num_blocks;
   int32_t num_kv_heads;
   int32_t num_q_heads;
@@ -602,10 +602,12 @@ void decode_kernel(DecodeArgs a) {
     if (single) {
       store_out<OutT>(reinterpret_cast<OutT*>(a.out) + row * D + d, val);
     } else {
-      a.part_o[(row * a.num_parts + part) * D + d] = val;
+      // One contiguous record per unit: its writes touch the fewest lines.
+      float* rec = a.part + (((int64_t)seq * a.num_kv_heads + g) * a.num_parts + part) * a.part_stride;
+      rec[hh * D + d] = val;
       if (d == 0) {
-        a.part_m[row * a.num_parts + part] = M;
-        a.part_l[row * a.num_parts + part] = den;
+        rec[G * D + hh] = M;
+        rec[G * D + G + hh] = den;
       }
     }
   }
@@ -627,10 +629,15 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   if ((int64_t)L > cap) L = (int)cap;
   const int n_parts = (L + a.ps - 1) / a.ps;
   if (n_parts <= 1) return;
-  const float* pm = a.part_m + row * a.num_parts;
-  const float* pl = a.part_l + row * a.num_parts;
+  const int h = (int)(row - (int64_t)seq * a.num_q_heads);
+  const int G = a.group;
+  const int g = h / G, hh = h - g * G;
+  const float* rec0 = a.part + ((int64_t)seq * a.num_kv_heads + g) * a.num_parts * a.part_stride;
+  const float* pm = rec0 + G * D + hh;            // m of partition p at pm[p * stride]
+  const float* pl = pm + G;
+  const int64_t stride = a.part_stride;
   float M = -INFINITY;
-  for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, pm[p]);
+  for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, pm[p * stride]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   constexpr int PER = D / kWave;           // dims per lane: 1 or 2
@@ -638,9 +645,9 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   float den = 0.f;
   if (M != -INFINITY) {
     for (int p = 0; p < n_parts; ++p) {
-      const float w = fast_exp2(pm[p] - M) * pl[p];
+      const float w = fast_exp2(pm[p * stride] - M) * pl[p * stride];
       den += w;
-      const float* op = a.part_o + (row * a.num_parts + p) * D;
+      const float* op = rec0 + p * stride + hh * D;
 #pragma unroll
       for (int e = 0; e < PER; ++e) num[e] += w * op[lane + e * kWave];
     }
@@ -673,11 +680,13 @@ static void geometry(int32_t max_len, int32_t partition_size, int32_t* ps, int32
   *parts = max_len > 0 ? (max_len + *ps - 1) / *ps : 1;
 }
 
-static size_t workspace_bytes(int64_t rows, int32_t parts, int32_t D) {
+// Floats per partial record: G rows of D, then G maxima and G sums, rounded up
+// to whole 128-byte lines.
+static int32_t record_floats(int32_t G, int32_t D) { return (G * D + 2 * G + 31) / 32 * 32; }
+
+static size_t workspace_bytes(int64_t units_per_part, int32_t parts, int32_t G, int32_t D) {
   if (parts <= 1) return 0;
-  const int64_t ml = rows * parts * 4;                      // m and l, fp32
-  const int64_t ml_pad = (ml + 255) / 256 * 256;
-  return (size_t)(2 * ml_pad + rows * parts * (int64_t)D * 4);
+  return (size_t)(units_per_part * parts * (int64_t)record_floats(G, D) * 4);
 }
 
 
@@ -714,7 +723,8 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   int32_t ps, parts;
   geometry(max_context_len, partition_size, &ps, &parts);
   const int64_t rows = (int64_t)num_seqs * num_q_heads;
-  const size_t need = workspace_bytes(rows, parts, pool->head_dim);
+  const size_t need = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts, G,
+                                      pool->head_dim);
   if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
   const int64_t units = (int64_t)pool->num_kv_heads * num_seqs * parts;
@@ -730,14 +740,8 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   a.out = out;
   a.tables = block_tables;
   a.lens = context_lens;
-  a.part_m = a.part_l = a.part_o = nullptr;
-  if (need > 0) {
-    const int64_t ml = rows * parts * 4;
-    const int64_t ml_pad = (ml + 255) / 256 * 256;
-    a.part_m = (float*)workspace;
-    a.part_l = (float*)((char*)workspace + ml_pad);
-    a.part_o = (float*)((char*)workspace + 2 * ml_pad);
-  }
+  a.part = need > 0 ? (float*)workspace : nullptr;
+  a.part_stride = record_floats(G, pool->head_dim);
   a.num_blocks = pool->num_blocks;
   a.num_kv_heads = pool->num_kv_heads;
   a.num_q_heads = num_q_heads;
@@ -784,10 +788,11 @@ pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
   if (st != PA_OK) return st;
   if (!bytes || num_seqs < 0 || num_q_heads < 1 || max_context_len < 0 || partition_size < 0)
     return PA_ERR_INVALID_ARG;
-  if (partition_size % kBlock) return PA_ERR_INVALID_ARG;
+  if (partition_size % kBlock || num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
   int32_t ps, parts;
   geometry(max_context_len, partition_size, &ps, &parts);
-  *bytes = workspace_bytes((int64_t)num_seqs * num_q_heads, parts, pool->head_dim);
+  *bytes = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts,
+                           num_q_heads / pool->num_kv_heads, pool->head_dim);
   return PA_OK;
 }
 

@@ -48,9 +48,10 @@ def test_workspace_size_host_only():
     st, n = B.pa_decode_workspace_size(d, 256, 32, 512, 512)
     assert st == B.PA_OK and n == 0                       # one partition: no partials
     st, n = B.pa_decode_workspace_size(d, 16, 64, 32768, 512)
-    rows, parts = 16 * 64, 64
-    pad = lambda x: (x + 255) // 256 * 256
-    assert st == B.PA_OK and n == 2 * pad(rows * parts * 4) + rows * parts * 128 * 4
+    units, parts, G = 16 * 8, 64, 8
+    rec = (G * 128 + 2 * G + 31) // 32 * 32          # floats, whole 128-byte lines
+    assert st == B.PA_OK and n == units * parts * rec * 4
+    assert B.pa_decode_workspace_size(d, 16, 60, 32768, 512)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, 500)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(_desc(head_dim=96), 1, 8, 16, 0)[0] == B.PA_ERR_UNSUPPORTED
     assert B.pa_decode_workspace_size(_desc(dtype="f32"), -1, 8, 16, 0)[0] == B.PA_ERR_INVALID_ARG
