@@ -48,7 +48,7 @@ def _workloads():
                                      "1024-token prompt + tails uniform 1..512"),
         "shared-prefix-bf16-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
                                      "1016-token prompt + tails uniform 1..512"),
-        "long-ctx-splitk-bf16": (W.long_ctx_bf16, 512, "uniform int 8192..32768"),
+        "long-ctx-splitk-bf16": (W.long_ctx_bf16, -1, "uniform int 8192..32768"),
         "tiny-f32": (W.tiny_f32, 0, "{50, 20, 65, 16}"),
     }
 
@@ -270,8 +270,8 @@ def main():
     ap.add_argument("--workload", default="gqa-bf16-b256", choices=sorted(_workloads()),
                     help="the headline metric is quoted on gqa-bf16-b256 (the default)")
     ap.add_argument("--partition", type=int, default=None,
-                    help="partition size in tokens (0 = one work unit per sequence and KV head; "
-                         "default: 0, or 512 for the long-context workload)")
+                    help="partition size in tokens (0 = one work unit per sequence and KV head, "
+                         "-1 = library's choice; default: 0, or -1 for the long-context workload)")
     ap.add_argument("--sweep", type=int, nargs="*", default=None,
                     help="time several partition sizes and report the fastest")
     ap.add_argument("--unfused", action="store_true",

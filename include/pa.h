@@ -90,6 +90,9 @@ enum {
 typedef int32_t pa_dtype;
 enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
 
+/* partition_size value asking the library to choose (see pa_decode_attention). */
+#define PA_PARTITION_AUTO (-1)
+
 /* Describes a K/V pool pair (layout above).  Passed by pointer, read only
  * during the call. */
 typedef struct pa_pool_desc {
@@ -180,12 +183,18 @@ PA_API pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_
  *   scale             multiplier of q.k (e.g. 1/sqrt(head_dim))
  *   max_context_len   host upper bound of every L_i (sizes the grid); lengths
  *                     above it are clipped to it
- *   partition_size    0: each (sequence, KV head) is one work unit; else
+ *   partition_size    0: each (sequence, KV head) is one work unit; > 0:
  *                     positions are split into consecutive partitions of
- *                     partition_size tokens (a positive multiple of
- *                     block_size), processed independently and combined by
- *                     a second kernel that rescales each partition's
- *                     (max, sum, weighted sum) to the global max
+ *                     partition_size tokens (a multiple of block_size),
+ *                     processed independently and combined by a second
+ *                     kernel that rescales each partition's (max, sum,
+ *                     weighted sum) to the global max; PA_PARTITION_AUTO:
+ *                     0 when num_seqs * Hkv already covers the GPU's
+ *                     resident workgroups (3 per compute unit of the current
+ *                     device), else about twice that many units, partitions
+ *                     of >= 512 tokens rounded to 256 (pa_decode_workspace_size
+ *                     with the same arguments on the same device gives the
+ *                     matching workspace)
  *   workspace         device, >= pa_decode_workspace_size bytes (may be NULL
  *                     when that size is 0)
  * Accumulation is fp32 in every dtype; q.k products of f16/bf16 inputs are

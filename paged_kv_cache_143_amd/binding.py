@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_PARTITION_AUTO = -1
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_slot_mapping", "pa_write_kv",

@@ -89,27 +89,93 @@ struct DecodeArgs {
 // Longest-first dispatch.  Workgroups start roughly in blockIdx order, so
 // giving consecutive indices to sequences in decreasing length (longest
 // processing time first) keeps the last workgroups to finish short.  Each
-// workgroup ranks the lengths itself, with unique keys (length, then lower
-// index first): rank(i) = #{j : key_j > key_i}.  O(S^2 / threads) compares.
-constexpr int kRankMax = 512;
+// workgroup finds the sequence of rank r itself by counting: a histogram of
+// block counts (descending; counts >= kRankBins - 1 share the last bin) in
+// LDS, a prefix scan that locates the bin holding rank r, then the position
+// within that bin in index order (ballots).  About six barriers and
+// O(S / threads + kRankBins / threads) work per thread.
+constexpr int kRankBins = 2048;
+constexpr int kRankLdsInts = kRankBins + kWaves + 3;
 
-__device__ inline int seq_of_rank(const int32_t* __restrict__ lens, int S, int r, uint32_t* keys) {
-  for (int i = threadIdx.x; i < S; i += blockDim.x) {
-    int L = lens[i];
-    L = L < 0 ? 0 : (L > (1 << 20) - 1 ? (1 << 20) - 1 : L);
-    keys[i] = ((uint32_t)L << 11) | (uint32_t)(2047 - i);
+__device__ inline int rank_bin(const DecodeArgs& a, int i) {
+  int L = a.lens[i];
+  L = L < 0 ? 0 : L;
+  L = L > a.max_len ? a.max_len : L;
+  const int64_t cap = (int64_t)a.max_blocks * kBlock;
+  if ((int64_t)L > cap) L = (int)cap;
+  int nb = (L + kBlock - 1) / kBlock;
+  nb = nb > kRankBins - 1 ? kRankBins - 1 : nb;
+  return kRankBins - 1 - nb;                   // longest first
+}
+
+__device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
+  static_assert(kRankBins % kThreads == 0, "bins per thread");
+  constexpr int kPer = kRankBins / kThreads;
+  int* hist = lds;
+  int* scratch = lds + kRankBins;              // [kWaves] partial counts, then results
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int w = t / kWave;
+  const int S = a.num_seqs;
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) hist[t * kPer + b] = 0;
+  __syncthreads();
+  for (int i = t; i < S; i += kThreads) atomicAdd(&hist[rank_bin(a, i)], 1);
+  __syncthreads();
+  // Exclusive prefix of the bin counts, kPer bins per thread.
+  int c = 0;
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) c += hist[t * kPer + b];
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) scratch[w] = incl;
+  __syncthreads();
+  int before = incl - c;
+  for (int v = 0; v < w; ++v) before += scratch[v];
+  if (r >= before && r < before + c) {         // the one thread whose bins hold rank r
+    int acc = before;
+    for (int b = 0; b < kPer; ++b) {
+      const int h = hist[t * kPer + b];
+      if (r < acc + h) {
+        scratch[kWaves] = t * kPer + b;
+        scratch[kWaves + 1] = r - acc;
+        break;
+      }
+      acc += h;
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < S; i += blockDim.x) {
-    const uint32_t ki = keys[i];
-    int rank = 0;
-    for (int j = 0; j < S; ++j) rank += keys[j] > ki ? 1 : 0;
-    if (rank == r) keys[kRankMax] = (uint32_t)i;
-  }
+  const int bin = scratch[kWaves];
+  int within = scratch[kWaves + 1];
   __syncthreads();
-  const int seq = (int)keys[kRankMax];
-  __syncthreads();                             // the keys area is reused afterwards
-  return seq;
+  // The `within`-th sequence (by index) of that bin.
+  for (int base = 0; base < S; base += kThreads) {
+    const int i = base + t;
+    const bool hit = i < S && rank_bin(a, i) == bin;
+    const unsigned long long m = __ballot(hit);
+    if (lane == 0) scratch[w] = __popcll(m);
+    __syncthreads();
+    int wbefore = 0, total = 0;
+    for (int v = 0; v < kWaves; ++v) {
+      wbefore += v < w ? scratch[v] : 0;
+      total += scratch[v];
+    }
+    if (within < total) {                      // uniform across the workgroup
+      const int mine = wbefore + __popcll(m & ((1ull << lane) - 1ull));
+      if (hit && mine == within) scratch[kWaves + 2] = i;
+      __syncthreads();
+      const int seq = scratch[kWaves + 2];
+      __syncthreads();                         // LDS is reused afterwards
+      return seq;
+    }
+    within -= total;
+    __syncthreads();
+  }
+  return 0;                                    // not reached: r < S
 }
 
 // ---- matrix-core wrappers -------------------------------------------------
@@ -456,8 +522,7 @@ void decode_kernel(DecodeArgs a) {
   const int rest = unit / a.num_kv_heads;
   const int part = rest / a.num_seqs;
   const int seq = a.longest_first
-                      ? seq_of_rank(a.lens, a.num_seqs, rest % a.num_seqs,
-                                    reinterpret_cast<uint32_t*>(smem))
+                      ? seq_of_rank(a, rest % a.num_seqs, reinterpret_cast<int*>(smem))
                       : rest % a.num_seqs;
 
   int L = a.lens[seq];
@@ -674,10 +739,33 @@ static pa_status dispatch_d(int D, const DecodeArgs& a, int64_t units, size_t ld
 }
 
 // Partition geometry shared by the size query and the launch.
-static void geometry(int32_t max_len, int32_t partition_size, int32_t* ps, int32_t* parts) {
+// Automatic partitioning: one unit per (sequence, KV head) already fills the
+// GPU when there are at least as many units as resident workgroups (3 per
+// compute unit); otherwise split so there are about twice that many, in
+// partitions of at least 512 tokens, a multiple of 256 (short units lose more
+// to their start-up latency than they gain in balance).
+static int32_t auto_partition(int64_t base_units, int32_t max_len) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * 3;
+  if (base_units >= slots || max_len <= 512) return 0;
+  const int64_t parts = (2 * slots + base_units - 1) / base_units;
+  int64_t ps = (max_len + parts - 1) / parts;
+  ps = (ps + 255) / 256 * 256;
+  return (int32_t)std::max<int64_t>(ps, 512);
+}
+
+static void geometry(int32_t max_len, int32_t partition_size, int64_t base_units, int32_t* ps,
+                     int32_t* parts) {
+  if (partition_size == PA_PARTITION_AUTO) partition_size = auto_partition(base_units, max_len);
   const int32_t whole = ((max_len > 0 ? max_len : 1) + kBlock - 1) / kBlock * kBlock;
   *ps = partition_size == 0 ? whole : partition_size;
   *parts = max_len > 0 ? (max_len + *ps - 1) / *ps : 1;
+}
+
+static bool partition_ok(int32_t partition_size) {
+  return partition_size == PA_PARTITION_AUTO || (partition_size >= 0 && partition_size % kBlock == 0);
 }
 
 // Floats per partial record: G rows of D, then G maxima and G sums, rounded up
@@ -701,12 +789,11 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0 || max_context_len < 0 ||
-      partition_size < 0)
+      !partition_ok(partition_size))
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
   const int32_t G = num_q_heads / pool->num_kv_heads;
   if (G > 16) return PA_ERR_UNSUPPORTED;
-  if (partition_size % kBlock) return PA_ERR_INVALID_ARG;
   if (out_dtype != PA_F32 && out_dtype != pool->dtype) return PA_ERR_UNSUPPORTED;
   const int es = elem_bytes(pool->dtype);
   if (k_new) {
@@ -721,8 +808,7 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   if (!(scale == scale)) return PA_ERR_INVALID_ARG;
 
   int32_t ps, parts;
-  geometry(max_context_len, partition_size, &ps, &parts);
-  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads, &ps, &parts);
   const size_t need = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts, G,
                                       pool->head_dim);
   if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
@@ -751,13 +837,13 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   a.max_len = max_context_len;
   a.ps = ps;
   a.num_parts = parts;
-  a.longest_first = num_seqs <= kRankMax ? 1 : 0;
+  a.longest_first = 1;
   a.qk_scale = scale * kLog2e;
   // LDS: [merge area | staged current token]; the ranking keys alias the start.
   const size_t merge = ((size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float) + 15) / 16 * 16;
   a.stage_off = (int32_t)merge;
   size_t lds = merge + (k_new ? (size_t)2 * pool->head_dim * es : 0);
-  if (a.longest_first) lds = std::max(lds, (size_t)(kRankMax + 1) * sizeof(uint32_t));
+  if (a.longest_first) lds = std::max(lds, (size_t)kRankLdsInts * sizeof(int));
   const hipStream_t s = (hipStream_t)stream;
   const int D = pool->head_dim;
 
@@ -786,11 +872,12 @@ pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
                                    int32_t partition_size, size_t* bytes) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
-  if (!bytes || num_seqs < 0 || num_q_heads < 1 || max_context_len < 0 || partition_size < 0)
+  if (!bytes || num_seqs < 0 || num_q_heads < 1 || max_context_len < 0 ||
+      !partition_ok(partition_size))
     return PA_ERR_INVALID_ARG;
-  if (partition_size % kBlock || num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
   int32_t ps, parts;
-  geometry(max_context_len, partition_size, &ps, &parts);
+  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads, &ps, &parts);
   *bytes = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts,
                            num_q_heads / pool->num_kv_heads, pool->head_dim);
   return PA_OK;

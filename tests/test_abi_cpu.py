@@ -52,6 +52,14 @@ def test_workspace_size_host_only():
     rec = (G * 128 + 2 * G + 31) // 32 * 32          # floats, whole 128-byte lines
     assert st == B.PA_OK and n == units * parts * rec * 4
     assert B.pa_decode_workspace_size(d, 16, 60, 32768, 512)[0] == B.PA_ERR_INVALID_ARG
+    # automatic partitioning (256 compute units when no device is visible; MI355X has 256)
+    auto = B.PA_PARTITION_AUTO
+    st, n = B.pa_decode_workspace_size(d, 256, 32, 2000, auto)
+    assert st == B.PA_OK and n == 0                # 2048 units already cover 768 slots
+    st, n = B.pa_decode_workspace_size(d, 16, 64, 32768, auto)
+    parts = -(-32768 // 2816)                      # 12 parts wanted -> 2731 -> 2816 tokens
+    assert st == B.PA_OK and n == 16 * 8 * parts * rec * 4
+    assert B.pa_decode_workspace_size(d, 16, 64, 32768, -2)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, 500)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(_desc(head_dim=96), 1, 8, 16, 0)[0] == B.PA_ERR_UNSUPPORTED
     assert B.pa_decode_workspace_size(_desc(dtype="f32"), -1, 8, 16, 0)[0] == B.PA_ERR_INVALID_ARG
