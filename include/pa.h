@@ -191,7 +191,7 @@ PA_API pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_
  *                     weighted sum) to the global max; PA_PARTITION_AUTO:
  *                     0 when num_seqs * Hkv already covers the GPU's
  *                     resident workgroups (3 per compute unit of the current
- *                     device), else about twice that many units, partitions
+ *                     device), else about 1.75 times that many units, partitions
  *                     of >= 512 tokens rounded to 256 (pa_decode_workspace_size
  *                     with the same arguments on the same device gives the
  *                     matching workspace)

@@ -96,6 +96,14 @@ struct DecodeArgs {
 // O(S / threads + kRankBins / threads) work per thread.
 constexpr int kRankBins = 2048;
 constexpr int kRankLdsInts = kRankBins + kWaves + 3;
+// Up to this many sequences, ranking by pairwise comparison (O(S^2 / threads),
+// two barriers) is cheaper than the counting selection's fixed cost.
+#ifndef PA_PAIRWISE_RANK_MAX
+#define PA_PAIRWISE_RANK_MAX 128
+#endif
+constexpr int kPairwiseRankMax = PA_PAIRWISE_RANK_MAX;
+
+
 
 __device__ inline int rank_bin(const DecodeArgs& a, int i) {
   int L = a.lens[i];
@@ -176,6 +184,23 @@ __device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
     __syncthreads();
   }
   return 0;                                    // not reached: r < S
+}
+
+// rank(i) = #{j : key_j > key_i} with unique keys (block count, then lower index).
+__device__ inline int seq_of_rank_pairwise(const DecodeArgs& a, int r, int* lds) {
+  const int S = a.num_seqs;
+  for (int i = threadIdx.x; i < S; i += kThreads) lds[i] = ((kRankBins - 1 - rank_bin(a, i)) << 12) | (4095 - i);
+  __syncthreads();
+  for (int i = threadIdx.x; i < S; i += kThreads) {
+    const int ki = lds[i];
+    int rank = 0;
+    for (int j = 0; j < S; ++j) rank += lds[j] > ki ? 1 : 0;
+    if (rank == r) lds[kPairwiseRankMax] = i;
+  }
+  __syncthreads();
+  const int seq = lds[kPairwiseRankMax];
+  __syncthreads();
+  return seq;
 }
 
 // ---- matrix-core wrappers -------------------------------------------------
@@ -521,9 +546,10 @@ void decode_kernel(DecodeArgs a) {
   const int g = unit % a.num_kv_heads;
   const int rest = unit / a.num_kv_heads;
   const int part = rest / a.num_seqs;
-  const int seq = a.longest_first
-                      ? seq_of_rank(a, rest % a.num_seqs, reinterpret_cast<int*>(smem))
-                      : rest % a.num_seqs;
+  const int seq = !a.longest_first ? rest % a.num_seqs
+                  : a.num_seqs <= kPairwiseRankMax
+                      ? seq_of_rank_pairwise(a, rest % a.num_seqs, reinterpret_cast<int*>(smem))
+                      : seq_of_rank(a, rest % a.num_seqs, reinterpret_cast<int*>(smem));
 
   int L = a.lens[seq];
   L = L < 0 ? 0 : L;
@@ -741,16 +767,17 @@ static pa_status dispatch_d(int D, const DecodeArgs& a, int64_t units, size_t ld
 // Partition geometry shared by the size query and the launch.
 // Automatic partitioning: one unit per (sequence, KV head) already fills the
 // GPU when there are at least as many units as resident workgroups (3 per
-// compute unit); otherwise split so there are about twice that many, in
+// compute unit); otherwise split so there are about 1.75 times that many, in
 // partitions of at least 512 tokens, a multiple of 256 (short units lose more
-// to their start-up latency than they gain in balance).
+// to their start-up latency than they gain in balance; measured on the
+// 16 x 8K..32K-token workload, 3072-token partitions).
 static int32_t auto_partition(int64_t base_units, int32_t max_len) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * 3;
   if (base_units >= slots || max_len <= 512) return 0;
-  const int64_t parts = (2 * slots + base_units - 1) / base_units;
+  const int64_t parts = (7 * slots + 4 * base_units - 1) / (4 * base_units);
   int64_t ps = (max_len + parts - 1) / parts;
   ps = (ps + 255) / 256 * 256;
   return (int32_t)std::max<int64_t>(ps, 512);
@@ -837,7 +864,11 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   a.max_len = max_context_len;
   a.ps = ps;
   a.num_parts = parts;
+#ifdef PA_NO_LONGEST_FIRST
+  a.longest_first = 0;
+#else
   a.longest_first = 1;
+#endif
   a.qk_scale = scale * kLog2e;
   // LDS: [merge area | staged current token]; the ranking keys alias the start.
   const size_t merge = ((size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float) + 15) / 16 * 16;

@@ -57,7 +57,7 @@ def test_workspace_size_host_only():
     st, n = B.pa_decode_workspace_size(d, 256, 32, 2000, auto)
     assert st == B.PA_OK and n == 0                # 2048 units already cover 768 slots
     st, n = B.pa_decode_workspace_size(d, 16, 64, 32768, auto)
-    parts = -(-32768 // 2816)                      # 12 parts wanted -> 2731 -> 2816 tokens
+    parts = -(-32768 // 3072)                      # 11 parts wanted -> 2979 -> 3072 tokens
     assert st == B.PA_OK and n == 16 * 8 * parts * rec * 4
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, -2)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, 500)[0] == B.PA_ERR_INVALID_ARG
