@@ -51,7 +51,8 @@
  *   Two separate pools, K and V, each num_blocks * Hkv tiles of
  *   block_size * head_dim elements; tile (blk, h) starts at element
  *   (blk * Hkv + h) * block_size * head_dim, so every (block, KV head) tile is
- *   one contiguous 4 KiB run for 16 x 128 16-bit or 16 x 64 fp32 elements.
+ *   one contiguous run: 4 KiB for 16 x 128 16-bit or 16 x 64 fp32 elements,
+ *   2 KiB at block_size 8, 8 KiB at block_size 32.
  *   Inside a tile:
  *     K: element (offset o, dim d) at o * head_dim + d
  *        -- token-major: one token's K is one contiguous row;
@@ -62,7 +63,7 @@
  *   K; 4 consecutive tokens of one dim of V), and a token write touches
  *   2 lines of K and 8 lines of V for 128 16-bit dims.
  *
- * Supported shapes: block_size 16; head_dim 64 or 128; dtype f32, f16, bf16;
+ * Supported shapes: block_size 8, 16 or 32; head_dim 64 or 128; dtype f32, f16, bf16;
  * 1 <= num_q_heads / num_kv_heads <= 16 and num_q_heads % num_kv_heads == 0.
  */
 #ifndef PA_H
@@ -97,7 +98,7 @@ enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
  * during the call. */
 typedef struct pa_pool_desc {
   int32_t num_blocks;    /* physical blocks in each pool, >= 1 */
-  int32_t block_size;    /* tokens per block (b); 16 */
+  int32_t block_size;    /* tokens per block (b); 8, 16 or 32 */
   int32_t num_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;      /* 64 or 128 */
   pa_dtype dtype;        /* element type of both pools */

@@ -180,7 +180,7 @@ def make_desc(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
     return PoolDesc(num_blocks, block_size, num_kv_heads, head_dim, DTYPE_CODES[dtype])
 
 
-def slot_mapping_t(block_tables, seq_ids, positions, slots, block_size: int = 16) -> None:
+def slot_mapping_t(block_tables, seq_ids, positions, slots, block_size: int) -> None:
     for t, nm in ((block_tables, "block_tables"), (seq_ids, "seq_ids"),
                   (positions, "positions"), (slots, "slots")):
         _dev_i32(t, nm)

@@ -37,15 +37,16 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t 
 
 // ---------------------------------------------------------------------------
 // Token writes.  One thread moves one 16-byte vector of X consecutive dims of
-// one (token, KV head).  K tiles are token-major ([16][d]): the vector is one
+// one (token, KV head).  K tiles are token-major ([b][d]): the vector is one
 // 16-byte store and a token's row is contiguous.  V tiles interleave groups of
-// 4 tokens per dim ([16/4][d][4]): X element stores, stride 4 elements.
+// 4 tokens per dim ([b/4][d][4]): X element stores, stride 4 elements.
 // ---------------------------------------------------------------------------
 template <int ES>  // element size in bytes: 2 or 4
 __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
                                 const char* __restrict__ k_new, const char* __restrict__ v_new,
                                 int64_t new_stride, const int32_t* __restrict__ slots, int32_t n,
-                                int32_t num_heads, int32_t head_dim, int64_t num_slots) {
+                                int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                int64_t num_slots) {
   constexpr int X = 16 / ES;
   const int chunks = head_dim / X;                 // vectors per (token, head)
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -57,10 +58,10 @@ __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_
   const int c = rem - h * chunks;
   const int32_t slot = slots[t];
   if (slot < 0 || (int64_t)slot >= num_slots) return;
-  const int32_t blk = slot / kBlock;
-  const int32_t off = slot - blk * kBlock;
+  const int32_t blk = slot / block_size;
+  const int32_t off = slot - blk * block_size;
   const int64_t src = ((int64_t)t * new_stride + (int64_t)h * head_dim + (int64_t)c * X) * ES;
-  const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)kBlock * head_dim;   // elements
+  const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)block_size * head_dim;  // elements
   const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + src);
   *reinterpret_cast<u32x4*>(k_pool + (tile + (int64_t)off * head_dim + (int64_t)c * X) * ES) = kv;
   const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + src);
@@ -105,18 +106,19 @@ __global__ void zero_int_kernel(int32_t* p) { *p = 0; }
 
 __global__ void validate_kernel(const int32_t* __restrict__ tables, int32_t max_blocks,
                                 const int32_t* __restrict__ lens, int32_t num_seqs,
-                                int32_t max_len, int32_t num_blocks, int32_t* bad) {
+                                int32_t max_len, int32_t num_blocks, int32_t block_size,
+                                int32_t* bad) {
   const int s = blockIdx.x;
   if (s >= num_seqs) return;
   const int32_t L = lens[s];
-  const int64_t cap = (int64_t)max_blocks * kBlock;
+  const int64_t cap = (int64_t)max_blocks * block_size;
   int32_t local = 0;
   int32_t check_blocks;
   if (L < 1 || L > max_len || (int64_t)L > cap) {
     if (threadIdx.x == 0) local += 1;
-    check_blocks = (L < 1) ? 0 : (int32_t)min<int64_t>((L + kBlock - 1) / kBlock, max_blocks);
+    check_blocks = (L < 1) ? 0 : (int32_t)min<int64_t>((L + block_size - 1) / block_size, max_blocks);
   } else {
-    check_blocks = (L + kBlock - 1) / kBlock;
+    check_blocks = (L + block_size - 1) / block_size;
   }
   for (int j = threadIdx.x; j < check_blocks; j += blockDim.x) {
     const int32_t phys = tables[(int64_t)s * max_blocks + j];
@@ -180,11 +182,11 @@ pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, cons
   if (es == 2)
     write_kv_kernel<2><<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
         (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
-        slot_mapping, n, pool->num_kv_heads, pool->head_dim, num_slots);
+        slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots);
   else
     write_kv_kernel<4><<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
         (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
-        slot_mapping, n, pool->num_kv_heads, pool->head_dim, num_slots);
+        slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots);
   return launch_status();
 }
 
@@ -221,7 +223,7 @@ pa_status pa_validate_tables(const pa_pool_desc* pool, const int32_t* block_tabl
   if (num_seqs > 0)
     validate_kernel<<<num_seqs, 256, 0, (hipStream_t)stream>>>(
         block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
-        pool->num_blocks, bad_count);
+        pool->num_blocks, pool->block_size, bad_count);
   return launch_status();
 }
 

@@ -49,6 +49,7 @@ namespace pa {
 #define PA_WAVES 4
 #endif
 constexpr int kWaves = PA_WAVES;
+constexpr int kRows = 16;           // tokens per matrix-core row tile (sub-tile)
 constexpr int kThreads = kWave * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -74,6 +75,9 @@ struct DecodeArgs {
                        // o/l [G][D], then m [G], then l [G], padded to 128 bytes
   int32_t part_stride; // floats per record
   int32_t num_blocks;
+  int32_t block_size;  // tokens per block: 8, 16 or 32
+  int32_t rows;        // tokens per 16-row sub-tile: min(block_size, 16)
+  int32_t sub;         // sub-tiles per block: block_size / rows
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t group;       // G = Hq / Hkv
@@ -109,9 +113,9 @@ __device__ inline int rank_bin(const DecodeArgs& a, int i) {
   int L = a.lens[i];
   L = L < 0 ? 0 : L;
   L = L > a.max_len ? a.max_len : L;
-  const int64_t cap = (int64_t)a.max_blocks * kBlock;
+  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
   if ((int64_t)L > cap) L = (int)cap;
-  int nb = (L + kBlock - 1) / kBlock;
+  int nb = (L + kRows - 1) / kRows;          // work measure: 16-token sub-tiles
   nb = nb > kRankBins - 1 ? kRankBins - 1 : nb;
   return kRankBins - 1 - nb;                   // longest first
 }
@@ -408,9 +412,10 @@ template <class Tag, int D> struct NewToken {
     *reinterpret_cast<u32x4*>(stage + (is_v ? D * ES : 0) + c * 16) = vec;
   }
 
+  // j: table entry of the block holding the token, o: its offset in the block.
   __device__ inline void store(const DecodeArgs& a, const int32_t* trow, int j, int g,
                                int o) const {
-    constexpr int64_t kTile = (int64_t)kBlock * D * ES;
+    const int64_t kTile = (int64_t)a.block_size * D * ES;
     const int t = threadIdx.x;
     if (t >= 2 * NC) return;
     const int phys = trow[j];
@@ -486,7 +491,7 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
                       lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     // Tail tokens of V are zeroed (their P is zero, but 0 * NaN is NaN).
     uint32_t keep0 = 0xffffffffu, keep1 = 0xffffffffu;
-    if (n_valid < kBlock) {
+    if (n_valid < kRows) {
       keep0 = (t0 + 0 < n_valid ? 0x0000ffffu : 0u) | (t0 + 1 < n_valid ? 0xffff0000u : 0u);
       keep1 = (t0 + 2 < n_valid ? 0x0000ffffu : 0u) | (t0 + 3 < n_valid ? 0xffff0000u : 0u);
     }
@@ -501,7 +506,7 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
       f32x4 va = f.v[n];
-      if (n_valid < kBlock) {
+      if (n_valid < kRows) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) va[e] = (t0 + e < n_valid) ? va[e] : 0.f;
       }
@@ -537,7 +542,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
 void decode_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   constexpr int ES = Elt<Tag>::bytes;
-  constexpr int64_t kTileBytes = (int64_t)kBlock * D * ES;
+  // A block of 32 tokens is two 16-row sub-tiles (each contiguous in both
+  // tile layouts); a block of 8 is one sub-tile whose rows 8..15 fall outside
+  // its buffer resource and read as zero.
+  const int64_t tile_bytes = (int64_t)a.block_size * D * ES;
+  const int sub_bytes = a.rows * D * ES;
   const int lane = threadIdx.x & (kWave - 1);
   // The wavefront index is uniform; saying so keeps the block loop scalar.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -554,7 +563,7 @@ void decode_kernel(DecodeArgs a) {
   int L = a.lens[seq];
   L = L < 0 ? 0 : L;
   L = L > a.max_len ? a.max_len : L;
-  const int64_t cap = (int64_t)a.max_blocks * kBlock;
+  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
   if ((int64_t)L > cap) L = (int)cap;
   const int n_parts = (L + a.ps - 1) / a.ps;
   const int G = a.group;
@@ -569,9 +578,10 @@ void decode_kernel(DecodeArgs a) {
   }
   if (part >= n_parts) return;
 
-  const int nblk_seq = (L + kBlock - 1) / kBlock;
-  const int j0 = part * (a.ps / kBlock);
-  const int j1 = min(nblk_seq, j0 + a.ps / kBlock);
+  // From here on j counts sub-tiles of `rows` tokens.
+  const int nsub_seq = (L + a.rows - 1) / a.rows;
+  const int j0 = part * (a.ps / a.rows);
+  const int j1 = min(nsub_seq, j0 + a.ps / a.rows);
   const int first = j0 + wave;
   const int cnt = first < j1 ? (j1 - first + kWaves - 1) / kWaves : 0;
 
@@ -586,12 +596,12 @@ void decode_kernel(DecodeArgs a) {
   for (int n = 0; n < D / 16; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
-  const int64_t head_tile = (int64_t)g * kTileBytes;
-  const int64_t block_stride = (int64_t)a.num_kv_heads * kTileBytes;
+  const int64_t head_tile = (int64_t)g * tile_bytes;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * tile_bytes;
 
   // Fused step: the unit holding position L-1 writes the current token.
-  const int j_new = (L - 1) / kBlock;
-  const int o_new = (L - 1) % kBlock;
+  const int j_new = (L - 1) / a.rows;          // its sub-tile
+  const int o_new = (L - 1) % a.rows;          // its register row
   const bool own_new = a.k_new != nullptr && j_new >= j0 && j_new < j1;
   char* stage = reinterpret_cast<char*>(smem) + a.stage_off;
   NewToken<Tag, D> tok;
@@ -611,11 +621,11 @@ void decode_kernel(DecodeArgs a) {
     int phys = __builtin_amdgcn_readlane(tb, min(i, n - 1));
     const int j = first + kWaves * (c0 + i);
     const bool ok = i < n && phys >= 0 && phys < a.num_blocks;
-    nv = ok ? min(kBlock, L - j * kBlock) : 0;
+    nv = ok ? min(a.rows, L - j * a.rows) : 0;
     if (!ok) phys = 0;
     if (own_new && j == j_new) nv = -nv;
-    const int64_t off = (int64_t)phys * block_stride + head_tile;
-    const int bytes = ok ? (int)kTileBytes : 0;
+    const int64_t off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
+    const int bytes = ok ? sub_bytes : 0;
     f.load(tile_rsrc(a.k_pool + off, bytes), tile_rsrc(a.v_pool + off, bytes), lane);
   };
   auto attend = [&](Frag<Tag, D>& f, int nv) {
@@ -627,7 +637,7 @@ void decode_kernel(DecodeArgs a) {
   };
   auto open_chunk = [&]() {
     n = min(kWave, cnt - c0);
-    tb = lane < n ? trow[first + kWaves * (c0 + lane)] : 0;
+    tb = lane < n ? trow[(first + kWaves * (c0 + lane)) / a.sub] : 0;
     load_into(fa, 0, nva);
   };
 
@@ -652,7 +662,7 @@ void decode_kernel(DecodeArgs a) {
   }
   // Pool write of the current token after the loop: a store while the same
   // tile streams in makes those loads wait on it.
-  if (own_new) tok.store(a, trow, j_new, g, o_new);
+  if (own_new) tok.store(a, trow, (L - 1) / a.block_size, g, (L - 1) % a.block_size);
 
   // ---- merge the four wavefronts (LDS) ----
   const float l_tot = xor_sum(st.l);
@@ -716,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   int L = a.lens[seq];
   L = L < 0 ? 0 : L;
   L = L > a.max_len ? a.max_len : L;
-  const int64_t cap = (int64_t)a.max_blocks * kBlock;
+  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
   if ((int64_t)L > cap) L = (int)cap;
   const int n_parts = (L + a.ps - 1) / a.ps;
   if (n_parts <= 1) return;
@@ -783,16 +793,16 @@ static int32_t auto_partition(int64_t base_units, int32_t max_len) {
   return (int32_t)std::max<int64_t>(ps, 512);
 }
 
-static void geometry(int32_t max_len, int32_t partition_size, int64_t base_units, int32_t* ps,
-                     int32_t* parts) {
+static void geometry(int32_t max_len, int32_t partition_size, int64_t base_units, int32_t b,
+                     int32_t* ps, int32_t* parts) {
   if (partition_size == PA_PARTITION_AUTO) partition_size = auto_partition(base_units, max_len);
-  const int32_t whole = ((max_len > 0 ? max_len : 1) + kBlock - 1) / kBlock * kBlock;
+  const int32_t whole = ((max_len > 0 ? max_len : 1) + b - 1) / b * b;
   *ps = partition_size == 0 ? whole : partition_size;
   *parts = max_len > 0 ? (max_len + *ps - 1) / *ps : 1;
 }
 
-static bool partition_ok(int32_t partition_size) {
-  return partition_size == PA_PARTITION_AUTO || (partition_size >= 0 && partition_size % kBlock == 0);
+static bool partition_ok(int32_t partition_size, int32_t b) {
+  return partition_size == PA_PARTITION_AUTO || (partition_size >= 0 && partition_size % b == 0);
 }
 
 // Floats per partial record: G rows of D, then G maxima and G sums, rounded up
@@ -816,7 +826,7 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0 || max_context_len < 0 ||
-      !partition_ok(partition_size))
+      !partition_ok(partition_size, pool->block_size))
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
   const int32_t G = num_q_heads / pool->num_kv_heads;
@@ -835,7 +845,8 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   if (!(scale == scale)) return PA_ERR_INVALID_ARG;
 
   int32_t ps, parts;
-  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads, &ps, &parts);
+  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads,
+           pool->block_size, &ps, &parts);
   const size_t need = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts, G,
                                       pool->head_dim);
   if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
@@ -856,6 +867,9 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   a.part = need > 0 ? (float*)workspace : nullptr;
   a.part_stride = record_floats(G, pool->head_dim);
   a.num_blocks = pool->num_blocks;
+  a.block_size = pool->block_size;
+  a.rows = std::min(pool->block_size, 16);
+  a.sub = pool->block_size / a.rows;
   a.num_kv_heads = pool->num_kv_heads;
   a.num_q_heads = num_q_heads;
   a.group = G;
@@ -904,11 +918,12 @@ pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (!bytes || num_seqs < 0 || num_q_heads < 1 || max_context_len < 0 ||
-      !partition_ok(partition_size))
+      !partition_ok(partition_size, pool->block_size))
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
   int32_t ps, parts;
-  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads, &ps, &parts);
+  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads,
+           pool->block_size, &ps, &parts);
   *bytes = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts,
                            num_q_heads / pool->num_kv_heads, pool->head_dim);
   return PA_OK;

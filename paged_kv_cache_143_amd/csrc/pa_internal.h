@@ -8,7 +8,6 @@
 
 namespace pa {
 
-constexpr int kBlock = 16;        // tokens per block (the only size built)
 constexpr int kWave = 64;         // CDNA wavefront width
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -27,7 +26,7 @@ inline pa_status check_pool(const pa_pool_desc* p) {
   if (p->num_blocks < 1 || p->block_size < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
     return PA_ERR_INVALID_ARG;
   if (!dtype_ok(p->dtype)) return PA_ERR_UNSUPPORTED;
-  if (p->block_size != kBlock) return PA_ERR_UNSUPPORTED;
+  if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32) return PA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
   // Flat slot indices are int32.
   if ((int64_t)p->num_blocks * p->block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;

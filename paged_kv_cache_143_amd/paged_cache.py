@@ -22,15 +22,13 @@ from . import binding as B
 from .blocks import BlockManager
 from .workloads import CREATE, FORK, APPEND, RELEASE, DTYPES, TABLE_PAD, Workload
 
-BLOCK = 16
-
-
 class PagedKV:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
-                 device: str = "cuda", poison: bool = True):
-        self.desc = B.make_desc(num_blocks, num_kv_heads, head_dim, dtype)
+                 device: str = "cuda", poison: bool = True, block_size: int = 16):
+        self.desc = B.make_desc(num_blocks, num_kv_heads, head_dim, dtype, block_size)
         self.dtype = dtype
-        elems = num_blocks * num_kv_heads * BLOCK * head_dim
+        self.block_size = block_size
+        elems = num_blocks * num_kv_heads * block_size * head_dim
         self.k = torch.empty(elems, dtype=DTYPES[dtype], device=device)
         self.v = torch.empty(elems, dtype=DTYPES[dtype], device=device)
         if poison:                                   # stale/unused slots read as NaN
@@ -88,7 +86,7 @@ class _Flusher:
             self.flush()
         self.writes.append((slot, key, row))
         self.write_slots.add(slot)
-        self.write_blocks.add(slot // BLOCK)
+        self.write_blocks.add(slot // self.kv.block_size)
 
     def add_copy(self, src: int, dst: int) -> None:
         if src in self.write_blocks or src in self.copy_dsts:
@@ -128,7 +126,7 @@ class _Flusher:
 
 def build_batch(w: Workload, device: str = "cuda", poison: bool = True,
                 table_width: Optional[int] = None, drop_payload_cache: bool = True) -> Batch:
-    kv = PagedKV(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, device, poison)
+    kv = PagedKV(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, device, poison, w.block_size)
     bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
     fl = _Flusher(w, kv, device)
     last: Dict[int, Tuple[int, int]] = {}
@@ -197,7 +195,8 @@ class DecodeStep:
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
     def write_current(self) -> None:
-        B.slot_mapping_t(self.b.tables, self.seq_ids, self.positions, self.slots)
+        B.slot_mapping_t(self.b.tables, self.seq_ids, self.positions, self.slots,
+                         self.b.kv.block_size)
         self.b.kv.write(self.k_new, self.v_new, self.slots)
 
     def attend(self) -> None:

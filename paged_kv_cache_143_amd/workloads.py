@@ -299,9 +299,18 @@ def long_ctx_bf16(num_seqs: int = 16, seed: int = 5, partition_size: int = 512) 
 
 def scaled(kind: str, seed: int, num_seqs: int, lo: int, hi: int, num_q_heads: int,
            num_kv_heads: int, head_dim: int, dtype: str, extra_blocks: float = 0.1,
-           partition_size: int = 0) -> Workload:
+           partition_size: int = 0, block_size: int = 16) -> Workload:
     """A reduced-size variant of a workload family (same distributions)."""
     rng = np.random.default_rng(seed + 100)
     lengths = _uniform_lengths(rng, num_seqs, lo, hi)
     return independent(kind, seed, dtype, lengths, num_q_heads, num_kv_heads, head_dim,
-                       _pool_for(lengths, 16, extra_blocks), partition_size=partition_size)
+                       _pool_for(lengths, block_size, extra_blocks), block_size=block_size,
+                       partition_size=partition_size)
+
+
+def gqa_bf16_block(block_size: int, num_seqs: int = 256, seed: int = 3) -> Workload:
+    """The batch-256 GQA workload (same lengths and values) on blocks of another size."""
+    rng = np.random.default_rng(seed + 100)
+    lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
+    return independent(f"gqa-bf16-b256-bs{block_size}", seed, "bf16", lengths, 32, 8, 128,
+                       _pool_for(lengths, block_size, 0.0), block_size=block_size)

@@ -7,9 +7,6 @@ import torch
 
 from paged_kv_cache_143_amd import binding as B
 
-BLOCK = 16
-
-
 _CONFIG = None
 
 
@@ -39,10 +36,11 @@ def require_gpu():
 def pool_logical(kv, num_kv_heads: int, head_dim: int):
     """Device pools -> fp64 CPU arrays [blocks][offset][head][dim], read through the
     pool layout of include/pa.h (K tiles [b][d]; V tiles [b/4][d][4])."""
-    nb = kv.k.numel() // (num_kv_heads * BLOCK * head_dim)
-    k = kv.k.view(nb, num_kv_heads, BLOCK, head_dim).permute(0, 2, 1, 3)
-    v = kv.v.view(nb, num_kv_heads, BLOCK // 4, head_dim, 4).permute(0, 2, 4, 1, 3)
-    v = v.reshape(nb, BLOCK, num_kv_heads, head_dim)
+    b = kv.block_size
+    nb = kv.k.numel() // (num_kv_heads * b * head_dim)
+    k = kv.k.view(nb, num_kv_heads, b, head_dim).permute(0, 2, 1, 3)
+    v = kv.v.view(nb, num_kv_heads, b // 4, head_dim, 4).permute(0, 2, 4, 1, 3)
+    v = v.reshape(nb, b, num_kv_heads, head_dim)
     return (k.to(torch.float64).cpu().numpy(), v.to(torch.float64).cpu().numpy())
 
 

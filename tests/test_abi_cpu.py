@@ -81,7 +81,7 @@ def test_host_argument_checks_launch_nothing():
     assert B.pa_write_kv(d, 18, 16, 16, 16, 1024, 16, 1, 0) == B.PA_ERR_INVALID_ARG
     # unsupported shapes
     assert B.pa_copy_blocks(_desc(head_dim=80), 16, 16, 16, 1, 0) == B.PA_ERR_UNSUPPORTED
-    bad_bs = B.PoolDesc(64, 8, 8, 128, B.PA_BF16)
+    bad_bs = B.PoolDesc(64, 24, 8, 128, B.PA_BF16)
     assert B.pa_copy_blocks(bad_bs, 16, 16, 16, 1, 0) == B.PA_ERR_UNSUPPORTED
     assert B.pa_copy_blocks(B.PoolDesc(64, 16, 8, 128, 7), 16, 16, 16, 1, 0) == B.PA_ERR_UNSUPPORTED
     assert B.pa_copy_blocks(B.PoolDesc(0, 16, 8, 128, 2), 16, 16, 16, 1, 0) == B.PA_ERR_INVALID_ARG

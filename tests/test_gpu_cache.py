@@ -65,7 +65,7 @@ def test_slot_mapping_bitexact(name):
             pos.append(p)
             want.append(paging.slot(run.tables[i], p, w.block_size))
     # out-of-range requests map to -1
-    bad = [(-1, 0), (S, 0), (0, -3), (0, M * 16), (0, M * 16 + 5)]
+    bad = [(-1, 0), (S, 0), (0, -3), (0, M * w.block_size), (0, M * w.block_size + 5)]
     for s, p in bad:
         seq.append(s)
         pos.append(p)
@@ -74,7 +74,7 @@ def test_slot_mapping_bitexact(name):
     seq_t = torch.tensor(seq, dtype=torch.int32, device=dev)
     pos_t = torch.tensor(pos, dtype=torch.int32, device=dev)
     out = torch.full((len(seq),), 12345, dtype=torch.int32, device=dev)
-    B.slot_mapping_t(batch.tables, seq_t, pos_t, out)
+    B.slot_mapping_t(batch.tables, seq_t, pos_t, out, w.block_size)
     got = out.cpu().numpy()
     assert np.array_equal(got, np.asarray(want, dtype=np.int32))
 
@@ -85,7 +85,7 @@ def test_slot_mapping_worked_example():
     seq = torch.zeros(3, dtype=torch.int32, device="cuda")
     pos = torch.tensor([50, 0, 63], dtype=torch.int32, device="cuda")
     out = torch.empty(3, dtype=torch.int32, device="cuda")
-    B.slot_mapping_t(tab, seq, pos, out)
+    B.slot_mapping_t(tab, seq, pos, out, 16)
     want = [paging.slot([7, 3, 12, 5], p, 16) for p in (50, 0, 63)]
     assert out.cpu().tolist() == want == [82, 112, 95]
 
