@@ -49,6 +49,12 @@ def _workloads():
         "shared-prefix-bf16-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
                                      "1016-token prompt + tails uniform 1..512"),
         "long-ctx-splitk-bf16": (W.long_ctx_bf16, -1, "uniform int 8192..32768"),
+        "gqa-bf16-b256-in-order": (W.gqa_bf16_in_order, 0,
+                                   "uniform int 200..2000, consecutive physical blocks"),
+        "gqa-bf16-b256-bs8": (lambda: W.gqa_bf16_block(8), 0,
+                              "uniform int 200..2000, 8-token blocks"),
+        "gqa-bf16-b256-bs32": (lambda: W.gqa_bf16_block(32), 0,
+                               "uniform int 200..2000, 32-token blocks"),
         "tiny-f32": (W.tiny_f32, 0, "{50, 20, 65, 16}"),
     }
 
@@ -82,7 +88,8 @@ def _algorithmic_bytes(w, lens, fused):
     kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * es
     q = w.num_seqs * w.num_q_heads * w.head_dim * es
     out = w.num_seqs * w.num_q_heads * w.head_dim * 4
-    tables = int(((L + 15) // 16).sum()) * 4 + w.num_seqs * 4
+    b = w.block_size
+    tables = int(((L + b - 1) // b).sum()) * 4 + w.num_seqs * 4
     new = 2 * (w.num_seqs * w.num_kv_heads * w.head_dim * 2 * es) if fused else 0
     return {"kv": kv, "q": q, "out": out, "tables_lens": tables, "new_tokens": new,
             "total": kv + q + out + tables + new}
@@ -94,7 +101,8 @@ def _walk_keys(pool, table, length):
 
 
 def cpu_baseline(w, budget_s: float):
-    """Time the fp64 oracle (as it stands) on leading sequences of the same batch."""
+    """Time the fp64 oracle (as it stands) on the same batch: whole passes over its
+    sequences until `budget_s` of oracle time, the last pass possibly partial."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -120,26 +128,48 @@ def cpu_baseline(w, budget_s: float):
 
     es = 4 if w.dtype == "f32" else 2
     with threadpool_limits(limits=1):
-        for i in range(w.num_seqs):
-            # materialise this sequence's payloads first: only the oracle is timed
-            for p in set(x[0] for x in _walk_keys(pool, tables[i], lens[i])):
-                resolve((p, 0))
-            t0 = time.perf_counter()
-            paged_decode(pool, resolve, tables, lens, q64, w.num_kv_heads, w.scale, rows=[i])
-            elapsed += time.perf_counter() - t0
-            if len(cache) > 4:
-                cache.clear()
-                w.drop_cache()
-            kv_bytes += lens[i] * w.num_kv_heads * w.head_dim * 2 * es
-            tokens += lens[i]
-            done += 1
-            if elapsed >= budget_s:
-                break
+        while elapsed < budget_s:
+            for i in range(w.num_seqs):
+                # materialise this sequence's payloads first: only the oracle is timed
+                for p in set(x[0] for x in _walk_keys(pool, tables[i], lens[i])):
+                    resolve((p, 0))
+                t0 = time.perf_counter()
+                paged_decode(pool, resolve, tables, lens, q64, w.num_kv_heads, w.scale, rows=[i])
+                elapsed += time.perf_counter() - t0
+                if len(cache) > 4:
+                    cache.clear()
+                    w.drop_cache()
+                kv_bytes += lens[i] * w.num_kv_heads * w.head_dim * 2 * es
+                tokens += lens[i]
+                done += 1
+                if elapsed >= budget_s:
+                    break
     return {"value": kv_bytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {w.num_seqs} sequences ({tokens} context tokens, all "
+            "sample": f"{done} sequence decodes = {done / w.num_seqs:.2f} passes over the "
+                      f"{w.num_seqs}-sequence batch ({tokens} context tokens, all "
                       f"{w.num_q_heads} query heads), fp64 NumPy oracle, 1 thread, "
                       f"{elapsed:.1f} s",
             "seconds": elapsed, "sequences": done}
+
+
+def device_copy_gbs(reps: int = 10) -> float:
+    """A plain 1 GiB device-to-device copy on the same GPU: (read + write bytes) /
+    median time.  The ceiling a bandwidth-bound kernel is compared with besides
+    the published peak."""
+    import numpy as np
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for k in range(reps):
+        dst.copy_(src)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    ms = np.median([ev[k].elapsed_time(ev[k + 1]) for k in range(reps)])
+    del src, dst
+    return 2 * (1 << 30) / (ms / 1e3) / 1e9
 
 
 def run(args):
@@ -218,6 +248,7 @@ def run(args):
     dec_mean_s = float(dec_ms.mean()) / 1e3
     achieved = alg["total"] / dec_mean_s / 1e9
     kv_gbs = alg["kv"] / (ms_step / 1e3) / 1e9
+    reserved = int(((lens + w.block_size - 1) // w.block_size).sum()) * w.block_size
     line = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + tokens/s at batch 256, 1 GPU",
         "value": round(kv_gbs, 1),
@@ -236,6 +267,7 @@ def run(args):
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "partition_size": ps, "out_dtype": "f32", "seed": w.seed,
+                   "reserved_tokens": reserved, "tail_waste_frac": round(1 - lens.sum() / reserved, 4),
                    "step": ("pa_slot_mapping + pa_write_kv(256 tokens) + pa_decode_attention"
                             if args.unfused else
                             "pa_decode_step (slot + write of 256 tokens + decode, one launch)")},
@@ -245,7 +277,9 @@ def run(args):
         "kernels_us": {"separate_write_and_slots_median":
                            round(float(np.median(write_ms)) * 1e3, 2) if args.unfused else 0.0,
                        "kv_launch_median": round(float(np.median(dec_ms)) * 1e3, 2),
-                       "kv_launch_mean": round(dec_mean_s * 1e6, 2)},
+                       "kv_launch_mean": round(dec_mean_s * 1e6, 2),
+                       "kv_launch_min": round(float(dec_ms.min()) * 1e3, 2),
+                       "kv_launch_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (_measured_traffic(not args.unfused, ps)
@@ -255,6 +289,9 @@ def run(args):
                                             else "") + ")",
                      "algorithmic_bytes": alg},
     }
+    copy = device_copy_gbs()
+    line["device_copy_gbs"] = round(copy, 1)
+    line["pct_device_copy"] = round(100.0 * kv_gbs / copy, 2)
     if args.sweep:
         line["sweep_ms_per_step"] = {str(p): round(v[0], 5) for p, v in results.items()}
     if not args.no_cpu_baseline:

@@ -140,7 +140,7 @@ def independent(name: str, seed: int, dtype: str, lengths: Sequence[int], num_q_
                 num_kv_heads: int, head_dim: int, num_blocks: int, block_size: int = 16,
                 pinned_first: Optional[Sequence[int]] = None, last_token_append: bool = True,
                 partition_size: int = 0, ghosts: Sequence[int] = (),
-                notes: str = "") -> Workload:
+                notes: str = "", in_order: bool = False) -> Workload:
     """Independent sequences (no sharing) on a seeded, shuffled free list.
 
     Sequence i is created with its first L_i - 1 tokens and then grows by one
@@ -148,12 +148,15 @@ def independent(name: str, seed: int, dtype: str, lengths: Sequence[int], num_q_
     the token written in the step itself.  `pinned_first` places those block
     ids at the end of the free list, in order, so the first sequence takes them.
     `ghosts` are lengths of earlier tenants that are created and released
-    first, so that recycled blocks hold their stale tokens.
+    first, so that recycled blocks hold their stale tokens.  `in_order` hands out
+    block ids 0, 1, 2, ... (each sequence's blocks then lie back to back: the
+    identity table, no indirection scatter) instead of a shuffled list.
     """
     rng = np.random.default_rng(seed)
     ids = list(range(num_blocks))
     pinned = list(pinned_first or [])
-    rest = _shuffled(rng, [i for i in ids if i not in set(pinned)])
+    rest = [i for i in ids if i not in set(pinned)]
+    rest = list(reversed(rest)) if in_order else _shuffled(rng, rest)
     free_order = rest + list(reversed(pinned))
     ops: List[Op] = []
     data_len: Dict[int, int] = {}
@@ -276,6 +279,15 @@ def gqa_bf16(num_seqs: int = 256, seed: int = 3) -> Workload:
     lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
     return independent("gqa-bf16-b256", seed, "bf16", lengths, 32, 8, 128,
                        _pool_for(lengths, 16, 0.0))
+
+
+def gqa_bf16_in_order(num_seqs: int = 256, seed: int = 3) -> Workload:
+    """The batch-256 GQA workload with every sequence on consecutive physical
+    blocks (same lengths and values): the cost of the table indirection."""
+    rng = np.random.default_rng(seed + 100)
+    lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
+    return independent("gqa-bf16-b256-in-order", seed, "bf16", lengths, 32, 8, 128,
+                       _pool_for(lengths, 16, 0.0), in_order=True)
 
 
 def shared_prefix_bf16(groups: int = 32, forks: int = 8, prompt_len: int = 1024,

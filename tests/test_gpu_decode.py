@@ -242,6 +242,7 @@ FULL = {
                             [0, 7, 8, 100, 255], 0),
     "shared-prefix-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
                             [0, 1, 7, 8, 130, 255], 32 * 7),
+    "gqa-in-order": (W.gqa_bf16_in_order, 0, [0, 100, 255], None),
     "long-ctx-splitk": (W.long_ctx_bf16, 512, [0, 5, 15], None),
     "long-ctx-auto": (W.long_ctx_bf16, -1, [1, 9, 14], None),
 }
