@@ -94,6 +94,9 @@ class Workload:
     data_len: Dict[int, int]       # payload key -> number of rows
     partition_size: int = 0
     notes: str = ""
+    # Multi-token workloads: the chunk of sequence i is its chunk_lens[i]
+    # newest tokens (payload rows L-n .. L-1 of key i); None for decode.
+    chunk_lens: Optional[List[int]] = None
     _cache: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = field(default_factory=dict, repr=False)
 
     @property
@@ -123,6 +126,13 @@ class Workload:
         rows = [normal((self.num_q_heads, self.head_dim), (self.seed, 3, n), self.dtype)
                 for n in self.seq_names]
         return torch.stack(rows) if rows else torch.empty(
+            (0, self.num_q_heads, self.head_dim), dtype=DTYPES[self.dtype])
+
+    def chunk_queries(self) -> torch.Tensor:
+        """q rows [sum(chunk_lens), Hq, d] of the chunks, sequence by sequence."""
+        rows = [normal((int(n), self.num_q_heads, self.head_dim), (self.seed, 4, name), self.dtype)
+                for name, n in zip(self.seq_names, self.chunk_lens)]
+        return torch.cat(rows) if rows else torch.empty(
             (0, self.num_q_heads, self.head_dim), dtype=DTYPES[self.dtype])
 
 
@@ -279,6 +289,34 @@ def gqa_bf16(num_seqs: int = 256, seed: int = 3) -> Workload:
     lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
     return independent("gqa-bf16-b256", seed, "bf16", lengths, 32, 8, 128,
                        _pool_for(lengths, 16, 0.0))
+
+
+def chunked(name: str, seed: int, dtype: str, prefix_lens: Sequence[int],
+            chunk_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
+            block_size: int = 16, extra_blocks: float = 0.1) -> Workload:
+    """Multi-token step: sequence i holds prefix_lens[i] computed tokens plus a
+    chunk of chunk_lens[i] new ones (prefill when the prefix is 0), all stored
+    in the pool (shuffled free list); the chunk's rows are the queries."""
+    lengths = [int(p) + int(c) for p, c in zip(prefix_lens, chunk_lens)]
+    w = independent(name, seed, dtype, lengths, num_q_heads, num_kv_heads, head_dim,
+                    _pool_for(lengths, block_size, extra_blocks), block_size=block_size,
+                    last_token_append=False)
+    w.chunk_lens = [int(c) for c in chunk_lens]
+    return w
+
+
+def prefill_bf16(num_seqs: int = 16, prompt_len: int = 2048, seed: int = 6) -> Workload:
+    """Whole-prompt prefill: 16 prompts of 2048 tokens, 32 q / 8 kv heads x 128, bf16."""
+    return chunked("prefill-bf16", seed, "bf16", [0] * num_seqs, [prompt_len] * num_seqs,
+                   32, 8, 128)
+
+
+def chunked_prefill_bf16(num_seqs: int = 32, chunk: int = 512, seed: int = 7) -> Workload:
+    """Chunked prefill: 32 sequences with cached prefixes U{512..4096} and a
+    512-token chunk each (a 16K-token step), 32 q / 8 kv heads x 128, bf16."""
+    rng = np.random.default_rng(seed + 100)
+    prefix = _uniform_lengths(rng, num_seqs, 512, 4096)
+    return chunked("chunked-prefill-bf16", seed, "bf16", prefix, [chunk] * num_seqs, 32, 8, 128)
 
 
 def gqa_bf16_in_order(num_seqs: int = 256, seed: int = 3) -> Workload:

@@ -11,6 +11,7 @@ import torch
 from oracle.allocator import BlockModel, run_script
 from oracle.pool import SlotPool
 from oracle import attention as OA
+from oracle import prefill as OPF
 
 
 class OracleRun:
@@ -45,6 +46,15 @@ class OracleRun:
         q = self.q64() if q is None else q
         return OA.paged_decode(self.pool, self.resolve, self.tables, self.lengths, q,
                                self.w.num_kv_heads, self.w.scale, rows=rows)
+
+    def chunk_q64(self) -> np.ndarray:
+        return self.w.chunk_queries().to(torch.float64).numpy()
+
+    def prefill(self, seqs: Optional[Sequence[int]] = None, q: Optional[np.ndarray] = None):
+        q = self.chunk_q64() if q is None else q
+        return OPF.paged_prefill(self.pool, self.resolve, self.tables, self.lengths,
+                                 self.w.chunk_lens, q, self.w.num_kv_heads, self.w.scale,
+                                 seqs=seqs)
 
     def logical_kv(self, i: int):
         return OA.gather_kv(self.pool, self.resolve, self.tables[i], self.lengths[i],
