@@ -35,7 +35,9 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 DEFAULT_PARTITION = 0
 COUNTERS = os.path.join(ROOT, "profiles", "decode_step_gqa_bf16_b256_counters.json")
 KERNEL_SOURCES = ("paged_kv_cache_143_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_143_amd/csrc/pa_tile.h",
                   "paged_kv_cache_143_amd/csrc/pa_internal.h")
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense, published
 
 
 # name -> (constructor, default partition size, length description, headline?)
@@ -56,6 +58,9 @@ def _workloads():
         "gqa-bf16-b256-bs32": (lambda: W.gqa_bf16_block(32), 0,
                                "uniform int 200..2000, 32-token blocks"),
         "tiny-f32": (W.tiny_f32, 0, "{50, 20, 65, 16}"),
+        "prefill-bf16": (W.prefill_bf16, 0, "16 prompts x 2048 tokens, no cached prefix"),
+        "chunked-prefill-bf16": (W.chunked_prefill_bf16, 0,
+                                 "32 x 512-token chunks over cached prefixes U{512..4096}"),
     }
 
 
@@ -172,6 +177,126 @@ def device_copy_gbs(reps: int = 10) -> float:
     return 2 * (1 << 30) / (ms / 1e3) / 1e9
 
 
+def _prefill_flops(w, lens, chunk_lens=None):
+    """Algorithmic flops of the chunks: per (row at position p, query head),
+    (p + 1) keys x (2d for q.k + 2d for P.V)."""
+    total = 0
+    for L, n in zip(lens, w.chunk_lens if chunk_lens is None else chunk_lens):
+        L, n = int(L), int(n)
+        keys = n * (L - n) + n * (n + 1) // 2            # sum over rows of (p + 1)
+        total += keys * w.num_q_heads * 4 * w.head_dim
+    return total
+
+
+def cpu_baseline_prefill(w, budget_s: float):
+    """The fp64 oracle (as it stands) on whole chunks of the same batch, sequence
+    by sequence, until `budget_s` of oracle time; flops as the GPU line counts them."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle.allocator import run_script
+    from oracle.attention import gather_kv
+    from oracle.pool import SlotPool
+    from oracle.prefill import causal_chunk
+
+    model = run_script(w.ops, w.num_blocks, w.block_size, w.free_order, checked=False)
+    pool = SlotPool(w.num_blocks, w.block_size)
+    pool.replay(model.events)
+    q = w.chunk_queries().to(torch.float64).numpy()
+    starts = [0]
+    for n in w.chunk_lens:
+        starts.append(starts[-1] + n)
+    elapsed, flops, rows = 0.0, 0, 0
+
+    def resolve(p):
+        k, v = w.kv(p[0])
+        return k[p[1]].to(torch.float64).numpy(), v[p[1]].to(torch.float64).numpy()
+
+    with threadpool_limits(limits=1):
+        for i, name in enumerate(w.seq_names):
+            L, n = model.length(name), w.chunk_lens[i]
+            K, V = gather_kv(pool, resolve, model.tables[name], L, w.num_kv_heads, w.head_dim)
+            t0 = time.perf_counter()
+            causal_chunk(q[starts[i]:starts[i + 1]], K, V, w.scale)
+            elapsed += time.perf_counter() - t0
+            flops += _prefill_flops(w, [L], [n])
+            rows += n
+            w.drop_cache()
+            if elapsed >= budget_s:
+                break
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{i + 1} of {w.num_seqs} chunks ({rows} rows, all {w.num_q_heads} "
+                      f"query heads), fp64 NumPy oracle, 1 thread, {elapsed:.1f} s",
+            "seconds": elapsed}
+
+
+def run_prefill(args, w, length_desc):
+    """Multi-token step: chunk K/V written (pa_slot_mapping + pa_write_kv), then
+    pa_prefill_attention; TFLOP/s of algorithmic flops over the whole step."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_143_amd.paged_cache import PrefillStep, build_batch
+
+    batch = build_batch(w, device="cuda")
+    lens = batch.bm.length_array(w.seq_names)
+    step = PrefillStep(batch)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev_w = [mk() for _ in range(args.steps)]
+    ev_a = [mk() for _ in range(args.steps)]
+    ev_end = mk()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev_w[k].record()
+        step.write_chunks()
+        ev_a[k].record()
+        step.attend()
+    ev_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nxt = [ev_w[k + 1] if k + 1 < args.steps else ev_end for k in range(args.steps)]
+    att_ms = np.array([ev_a[k].elapsed_time(nxt[k]) for k in range(args.steps)])
+    wr_ms = np.array([ev_w[k].elapsed_time(ev_a[k]) for k in range(args.steps)])
+    ms_step = wall / args.steps * 1e3
+    flops = _prefill_flops(w, lens)
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    att_tf = flops / (att_ms.mean() / 1e3) / 1e12
+    value = flops / (ms_step / 1e3) / 1e12
+    rows = int(sum(w.chunk_lens))
+    print(f"[bench] prefill step {ms_step:.4f} ms, attention launch median "
+          f"{np.median(att_ms) * 1e3:.1f} us, chunk write median {np.median(wr_ms) * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": "paged prefill attention TFLOP/s (algorithmic, causal) + rows/s, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "num_seqs": w.num_seqs, "chunks": length_desc,
+                   "rows": rows, "context_tokens": int(lens.sum()),
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "out_dtype": "f32",
+                   "seed": w.seed,
+                   "step": "pa_slot_mapping + pa_write_kv(chunk rows) + pa_prefill_attention"},
+        "rows_per_s": round(rows / (ms_step / 1e3), 1),
+        "kernels_us": {"chunk_write_median": round(float(np.median(wr_ms)) * 1e3, 2),
+                       "attention_median": round(float(np.median(att_ms)) * 1e3, 2),
+                       "attention_mean": round(float(att_ms.mean()) * 1e3, 2),
+                       "attention_min": round(float(att_ms.min()) * 1e3, 2),
+                       "attention_p90": round(float(np.percentile(att_ms, 90)) * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(att_tf, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(att_tf / peak, 4), "traffic": None,
+                     "kernel": "pa_prefill_attention (prefill_kernel)",
+                     "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def run(args):
     import numpy as np
     import torch
@@ -194,6 +319,8 @@ def run(args):
         del src, dst
     make, default_ps, length_desc = _workloads()[args.workload]
     w = make()
+    if w.chunk_lens is not None:
+        return run_prefill(args, w, length_desc)
     if args.partition is None:
         args.partition = default_ps
     t_setup = time.perf_counter()

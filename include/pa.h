@@ -238,6 +238,37 @@ PA_API pa_status pa_decode_step(const pa_pool_desc* pool, void* k_pool, void* v_
                                 void* stream);
 
 /*
+ * pa_prefill_attention -- multi-token (prefill or chunked-prefill) attention
+ * through the block tables.  Sequence i stores L_i tokens; its chunk is the
+ * n_i newest of them, n_i = q_start[i+1] - q_start[i] (positions L_i - n_i ..
+ * L_i - 1, their K/V already written, e.g. by pa_write_kv).  Chunk row t sits
+ * at position p = L_i - n_i + t and attends causally to positions 0 .. p:
+ *     out[q_start[i] + t][h] = sum_{k <= p} softmax_k(scale * q[..][h] . K_i[k][g]) V_i[k][g]
+ * with g = h / G as in decode.  In prefill all prompt tokens are known at once
+ * (transcript, paragraph 1); a long prompt is processed in chunks over the
+ * cached earlier tokens ("Inside vLLM and TGI", sections "Read the vLLM0.11.0
+ * scheduler" and "Observability and debugging runbook").  n_i = L_i is a
+ * whole prompt; n_i = 1 is one decode query.
+ *   q              device [T][Hq][head_dim], pool dtype, 16-byte aligned;
+ *                  T = q_start[num_seqs]
+ *   out            device [T][Hq][head_dim] of out_dtype (PA_F32 or the pool
+ *                  dtype), 16-byte aligned
+ *   q_start        device int32 [num_seqs + 1], non-decreasing, q_start[0] = 0
+ *   max_chunk_len  >= every n_i (host value; sizes the grid).  Rows of a
+ *                  chunk past it are not computed.
+ *   other arguments as pa_decode_attention (lengths clipped the same way).
+ * A row with p < 0 (n_i > L_i) gets zeros.  Accumulation is fp32; P is split
+ * into high and low 16-bit parts for the P.V products as in decode.
+ */
+PA_API pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_pool,
+                                      const void* v_pool, const void* q, void* out,
+                                      pa_dtype out_dtype, const int32_t* q_start,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, float scale, int32_t max_chunk_len,
+                                      int32_t max_context_len, void* stream);
+
+/*
  * pa_validate_tables -- debug check of device-resident tables before a
  * kernel consumes them ("Inside vLLM and TGI", section "Exact CPU block
  * manager and copy-on-write", validation paragraph).  Counts violations:

@@ -22,7 +22,7 @@ DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_attention",
-           "pa_decode_step", "pa_validate_tables")
+           "pa_decode_step", "pa_prefill_attention", "pa_validate_tables")
 
 
 class PaError(RuntimeError):
@@ -82,10 +82,12 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_attention.restype = I32
     L.pa_decode_attention.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I32, P, I32, P,
                                       I32, I32, ctypes.c_float, I32, I32, P, ctypes.c_size_t, P]
-    if hasattr(L, "pa_decode_step"):          # absent from builds older than the fused step
-        L.pa_decode_step.restype = I32
-        L.pa_decode_step.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I64, P, P, I32, P, I32,
-                                     P, I32, I32, ctypes.c_float, I32, I32, P, ctypes.c_size_t, P]
+    L.pa_decode_step.restype = I32
+    L.pa_decode_step.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I64, P, P, I32, P, I32,
+                                 P, I32, I32, ctypes.c_float, I32, I32, P, ctypes.c_size_t, P]
+    L.pa_prefill_attention.restype = I32
+    L.pa_prefill_attention.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I32, P, P, I32, P,
+                                       I32, I32, ctypes.c_float, I32, I32, P]
     L.pa_validate_tables.restype = I32
     L.pa_validate_tables.argtypes = [ctypes.POINTER(PoolDesc), P, I32, P, I32, I32, P, P]
     return L
@@ -150,6 +152,15 @@ def pa_decode_step(desc, k_pool, v_pool, k_new, v_new, new_stride, q, out, out_d
                                 out, out_dtype, block_tables, max_blocks_per_seq, context_lens,
                                 num_seqs, num_q_heads, scale, max_context_len, partition_size,
                                 workspace, workspace_bytes, stream)
+
+
+def pa_prefill_attention(desc, k_pool, v_pool, q, out, out_dtype, q_start, block_tables,
+                         max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale,
+                         max_chunk_len, max_context_len, stream) -> int:
+    return lib().pa_prefill_attention(ctypes.byref(desc), k_pool, v_pool, q, out, out_dtype,
+                                      q_start, block_tables, max_blocks_per_seq, context_lens,
+                                      num_seqs, num_q_heads, scale, max_chunk_len,
+                                      max_context_len, stream)
 
 
 def pa_validate_tables(desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
@@ -255,6 +266,27 @@ def decode_step_t(desc, k_pool, v_pool, k_new, v_new, q, out, block_tables, cont
                           block_tables.shape[1], _ptr(context_lens), S, Hq, float(scale),
                           int(max_context_len), int(partition_size), _ptr(workspace), ws_bytes,
                           _stream()))
+
+
+def prefill_attention_t(desc, k_pool, v_pool, q, out, q_start, block_tables, context_lens, scale,
+                        max_chunk_len, max_context_len) -> None:
+    import torch
+    _dev_i32(q_start, "q_start")
+    _dev_i32(block_tables, "block_tables")
+    _dev_i32(context_lens, "context_lens")
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    if q.shape != out.shape:
+        raise ValueError("out must have q's shape")
+    S, M = block_tables.shape
+    if q_start.numel() != S + 1 or context_lens.numel() != S:
+        raise ValueError("q_start needs num_seqs + 1 entries, context_lens num_seqs")
+    out_code = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[out.dtype]
+    _check("pa_prefill_attention",
+           pa_prefill_attention(desc, _ptr(k_pool), _ptr(v_pool), _ptr(q), _ptr(out), out_code,
+                                _ptr(q_start), _ptr(block_tables), M, _ptr(context_lens), S,
+                                q.shape[1], float(scale), int(max_chunk_len),
+                                int(max_context_len), _stream()))
 
 
 def validate_tables_t(desc, block_tables, context_lens, max_context_len, bad_count) -> None:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_cache.hip", "pa_decode.hip"]
+SOURCES = ["pa_cache.hip", "pa_decode.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for all device code.

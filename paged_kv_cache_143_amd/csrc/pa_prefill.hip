@@ -1,0 +1,264 @@
+// Multi-token (prefill and chunked-prefill) paged attention for gfx950 (MI355X).
+//
+// What it computes: sequence i holds L_i tokens in the pool; its chunk is the
+// n_i newest of them (positions L_i - n_i .. L_i - 1, K/V already written).
+// Chunk row t (position p = L_i - n_i + t), query head h, KV head g = h / G:
+//     out[t][h] = sum_{k <= p} softmax_k(scale * q[t][h] . K_i[k][g]) V_i[k][g],
+// K_i[k] read through block table i as in decode.  In prefill every prompt
+// token is known at once, so the work is a dense matrix product
+// ("vLLM and PagedAttention: Virtual Memory for LLM Serving", paragraph 1);
+// long prompts are processed in chunks whose older tokens are already cached
+// ("Inside vLLM and TGI: Paging, Versioned Schedulers and Operations",
+// sections "Read the vLLM0.11.0 scheduler" and "Observability and debugging
+// runbook").  The pages give no formula; this is causal scaled dot-product
+// attention read through the table.
+//
+// Work decomposition.  A column is one (chunk row, query head of group g)
+// pair; a 16-column group packs floor(16 / G) consecutive rows times the G
+// heads of the group.  A wavefront owns NQ column groups and walks the
+// sequence's 16-token sub-tiles from position 0 up to its last row's
+// position, with the same registers-only pipeline as decode: K and V
+// fragments loaded straight from the pool layout one sub-tile ahead,
+// S^T = K q^T on the matrix cores, a causal mask per column, online softmax,
+// O^T += V^T P^T with P split into high and low 16-bit halves.  Each K/V
+// fragment serves NQ groups; the four wavefronts of a workgroup take
+// consecutive row ranges of one (sequence, KV head) and re-read the same
+// tiles, which the L2 serves (cached loads, unlike decode's streaming ones).
+// Workgroups run the chunk's last rows (the most keys) first.
+#include <algorithm>
+
+#include "pa_tile.h"
+
+namespace pa {
+
+constexpr int kPWaves = 4;
+constexpr int kPThreads = kWave * kPWaves;
+
+#ifndef PA_PREFILL_NQ
+#define PA_PREFILL_NQ 2
+#endif
+constexpr int kNQ = PA_PREFILL_NQ;
+
+struct PrefillArgs {
+  const char* k_pool;
+  const char* v_pool;
+  const char* q;             // [T][Hq][D]
+  void* out;                 // [T][Hq][D]
+  const int32_t* q_start;    // [S + 1]: first row of each sequence's chunk
+  const int32_t* tables;
+  const int32_t* lens;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t rows;              // tokens per sub-tile: min(block_size, 16)
+  int32_t sub;               // sub-tiles per block
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t group;             // G
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t max_len;
+  int32_t tpg;               // chunk rows per 16-column group: 16 / G
+  int32_t wave_rows;         // NQ * tpg
+  int32_t num_tiles;         // row tiles of kPWaves * wave_rows per sequence
+  float qk_scale;            // scale * log2(e)
+};
+
+template <class Tag, int D, int NQ, class OutT>
+__global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
+  constexpr int ES = Elt<Tag>::bytes;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  const int unit = blockIdx.x;
+  const int g = unit % a.num_kv_heads;
+  const int rest = unit / a.num_kv_heads;
+  const int seq = rest % a.num_seqs;
+  const int tile = a.num_tiles - 1 - rest / a.num_seqs;
+
+  const int qs = a.q_start[seq];
+  const int n = a.q_start[seq + 1] - qs;
+  int L = a.lens[seq];
+  L = L < 0 ? 0 : L;
+  L = L > a.max_len ? a.max_len : L;
+  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
+  if ((int64_t)L > cap) L = (int)cap;
+
+  const int row0 = (tile * kPWaves + wave) * a.wave_rows;   // this wavefront's first chunk row
+  if (row0 >= n) return;                                     // no barriers below
+  const int row_end = min(n, row0 + a.wave_rows);
+  const int G = a.group;
+  const int head0 = g * G;
+
+  // Columns: lane c (= lane % 16) of group q is chunk row row0 + q*tpg + c/G,
+  // head head0 + c%G; columns past tpg*G or past the chunk are idle.
+  const int c = lane & 15;
+  const int cr = c / G;
+  const int chh = c - cr * G;
+  const bool col_ok = c < a.tpg * G;
+  QFrag<Tag, D> qf[NQ];
+  int pos[NQ];
+  bool has[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int t = row0 + q * a.tpg + cr;
+    const int p = L - n + t;
+    has[q] = col_ok && t < row_end && p >= 0;
+    pos[q] = has[q] ? p : 0;              // idle columns see key 0 only (their q is 0)
+    const int64_t qrow = has[q] ? ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) : 0;
+    qf[q].load(a.q + qrow * D * ES, has[q], lane);
+  }
+
+  // Keys 0 .. p_last, where p_last is the position of the wavefront's last row.
+  const int p_last = L - n + row_end - 1;
+  State<D> st[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    st[q].m = -INFINITY;
+    st[q].l = 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) st[q].acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int64_t tile_bytes = (int64_t)a.block_size * D * ES;
+  const int sub_bytes = a.rows * D * ES;
+  const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
+  const int64_t head_tile = (int64_t)g * tile_bytes;
+  const int64_t block_stride = (int64_t)a.num_kv_heads * tile_bytes;
+  const int cnt = p_last >= 0 ? p_last / a.rows + 1 : 0;    // sub-tiles to walk
+
+  Frag<Tag, D> fa, fb;
+  int nva = 0, nvb = 0;
+  int c0 = 0, nc = 0, tb = 0;
+  auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
+    int phys = __builtin_amdgcn_readlane(tb, min(i, nc - 1));
+    const int j = c0 + i;
+    const bool ok = i < nc && phys >= 0 && phys < a.num_blocks;
+    nv = ok ? min(a.rows, L - j * a.rows) : 0;
+    if (!ok) phys = 0;
+    const int64_t off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
+    const int bytes = ok ? sub_bytes : 0;
+    f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
+                                   tile_rsrc(a.v_pool + off, bytes), lane);
+  };
+  auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
+    if (nv <= 0) return;
+    const int key0 = (c0 + i) * a.rows;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      attend_block<Tag, D, true>(f, qf[q], st[q], nv, a.qk_scale, lane, pos[q] - key0 + 1);
+  };
+  auto open_chunk = [&]() {
+    nc = min(kWave, cnt - c0);
+    tb = lane < nc ? trow[(c0 + lane) / a.sub] : 0;
+    load_into(fa, 0, nva);
+  };
+
+  for (; c0 < cnt; c0 += kWave) {
+    open_chunk();
+    for (int i = 0; i < nc; i += 2) {
+      load_into(fb, i + 1, nvb);
+      attend(fa, nva, i);
+      if (i + 1 >= nc) break;
+      load_into(fa, i + 2, nva);
+      attend(fb, nvb, i + 1);
+    }
+  }
+
+  // Normalise and store: lane holds dims 16k + 4(lane/16) .. +3 of its column.
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const float l_tot = xor_sum(st[q].l);
+    const int t = row0 + q * a.tpg + cr;
+    if (!(col_ok && t < row_end)) continue;
+    const float inv = (has[q] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    OutT* o = reinterpret_cast<OutT*>(a.out) +
+              ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store_out<OutT>(o + 16 * k + r, st[q].acc[k][r] * inv);
+  }
+}
+
+template <class Tag, int D, class OutT>
+static pa_status launch_prefill(const PrefillArgs& a, int64_t units, hipStream_t s) {
+  prefill_kernel<Tag, D, kNQ, OutT><<<(unsigned)units, kPThreads, 0, s>>>(a);
+  return launch_status();
+}
+
+template <class Tag, class OutT>
+static pa_status dispatch_prefill(int D, const PrefillArgs& a, int64_t units, hipStream_t s) {
+  if (D == 128) return launch_prefill<Tag, 128, OutT>(a, units, s);
+  return launch_prefill<Tag, 64, OutT>(a, units, s);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
+                               const void* q, void* out, pa_dtype out_dtype,
+                               const int32_t* q_start, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, float scale,
+                               int32_t max_chunk_len, int32_t max_context_len, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 0 || max_context_len < 0 ||
+      max_chunk_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  if (G > 16) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != pool->dtype) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_chunk_len == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !out || !q_start || !context_lens) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(q) || !aligned16(out))
+    return PA_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PA_ERR_INVALID_ARG;
+
+  PrefillArgs a;
+  a.k_pool = (const char*)k_pool;
+  a.v_pool = (const char*)v_pool;
+  a.q = (const char*)q;
+  a.out = out;
+  a.q_start = q_start;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.num_blocks = pool->num_blocks;
+  a.block_size = pool->block_size;
+  a.rows = std::min(pool->block_size, 16);
+  a.sub = pool->block_size / a.rows;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = G;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_len = max_context_len;
+  a.tpg = 16 / G;
+  a.wave_rows = kNQ * a.tpg;
+  const int32_t wg_rows = kPWaves * a.wave_rows;
+  a.num_tiles = (max_chunk_len + wg_rows - 1) / wg_rows;
+  a.qk_scale = scale * 1.4426950408889634f;
+  const int64_t units = (int64_t)a.num_kv_heads * num_seqs * a.num_tiles;
+  if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const hipStream_t s = (hipStream_t)stream;
+  const int D = pool->head_dim;
+  switch (pool->dtype) {
+    case PA_BF16:
+      return out_dtype == PA_F32 ? dispatch_prefill<TagBF16, float>(D, a, units, s)
+                                 : dispatch_prefill<TagBF16, __bf16>(D, a, units, s);
+    case PA_F16:
+      return out_dtype == PA_F32 ? dispatch_prefill<TagF16, float>(D, a, units, s)
+                                 : dispatch_prefill<TagF16, _Float16>(D, a, units, s);
+    case PA_F32:
+      return dispatch_prefill<TagF32, float>(D, a, units, s);
+    default:
+      return PA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // extern "C"

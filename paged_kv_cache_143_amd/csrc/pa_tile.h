@@ -1,0 +1,253 @@
+// Matrix-core tile code shared by the decode and prefill kernels (gfx950):
+// MFMA wrappers, the per-sub-tile K/V register fragments read straight from
+// the pool layout, the query fragment, and one online-softmax step over a
+// 16-token sub-tile.
+//
+// Roles (v_mfma_f32_16x16x32_{bf16,f16}; fp32 pools: 16x16x4_f32):
+//   S^T = K q^T: A = K sub-tile (16 tokens as rows), B = q (16 query columns),
+//   C = 16 tokens x 16 columns, lane (c + 16 g) holding tokens 4g..4g+3 of
+//   column c -- which is exactly the B-operand layout of
+//   O^T += V^T P^T, so P never moves between lanes.
+#pragma once
+
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kRows = 16;           // tokens per matrix-core row tile (sub-tile)
+
+struct TagF32 {};
+struct TagF16 {};
+struct TagBF16 {};
+
+template <class Tag> struct Is16 { static constexpr bool value = true; };
+template <> struct Is16<TagF32> { static constexpr bool value = false; };
+
+// ---- matrix-core wrappers -------------------------------------------------
+template <class Tag> __device__ inline f32x4 mma32(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ inline f32x4 mma32<TagBF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ inline f32x4 mma32<TagF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even narrowing of p to 16 bits, and the residual.
+template <class Tag> __device__ inline uint32_t narrow16(float x);
+template <> __device__ inline uint32_t narrow16<TagBF16>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+template <> __device__ inline uint32_t narrow16<TagF16>(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+template <class Tag> __device__ inline float widen16(uint32_t bits);
+template <> __device__ inline float widen16<TagBF16>(uint32_t bits) {
+  return __builtin_bit_cast(float, bits << 16);
+}
+template <> __device__ inline float widen16<TagF16>(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ inline float xor_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---- per-block register fragments ------------------------------------------
+// 16-bit: K tile [16][d] -> load m gives lane (t = lane%16) the 8 dims
+// 8*(4m + lane/16) .. of its token (16 bytes); V tile [16/4][d][4] -> load n
+// gives lane (d = 16n + lane%16) the 4 tokens 4*(lane/16) .. of that dim
+// (8 bytes; each instruction reads four full 128-byte lines).
+template <class Tag, int D, bool H = Is16<Tag>::value> struct Frag;
+
+// Each tile is read through its own buffer resource (base = tile address,
+// size = tile bytes); a resource of size 0 makes every lane's access out of
+// range, which returns zeros without touching memory -- the one-block-ahead
+// prefetch uses that past a wavefront's last block, so its wait counts stay
+// static without a spare read of real data.  Decode reads each tile once per
+// call: streaming (non-temporal) loads; prefill re-reads tiles across query
+// tiles: ordinary cached loads.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;         // raw (untyped) buffer, gfx9 family
+#ifndef PA_TEMPORAL_KV
+#define PA_TEMPORAL_KV 0
+#endif
+constexpr int kPolicyCached = 0;
+constexpr int kPolicyStream = 2;               // nt
+constexpr int kKvCachePolicy = PA_TEMPORAL_KV ? kPolicyCached : kPolicyStream;
+
+__device__ inline rsrc_t tile_rsrc(const char* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), 0, bytes, kRsrcWord3);
+}
+template <int Pol = kKvCachePolicy> __device__ inline u32x4 buf_load16(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, Pol);
+}
+template <int Pol = kKvCachePolicy> __device__ inline u32x2 buf_load8(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, Pol);
+}
+
+template <class Tag, int D> struct Frag<Tag, D, true> {
+  static constexpr int NK = D / 32;
+  static constexpr int NV = D / 16;
+  u32x4 k[NK];
+  u32x2 v[NV];
+  template <int Pol = kKvCachePolicy>
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
+    const int kr = (lane & 15) * (D * 2) + (lane >> 4) * 16;
+#pragma unroll
+    for (int m = 0; m < NK; ++m) k[m] = buf_load16<Pol>(rk, kr + m * 64);
+    const int vr = (lane >> 4) * (D * 8) + (lane & 15) * 8;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) v[n] = buf_load8<Pol>(rv, vr + n * 128);
+  }
+};
+
+// fp32: K tile [16][d] -> load j gives lane (t = lane%16) dims
+// 4*(4j + lane/16) ..; V tile [16/4][d][4] -> load n gives lane
+// (d = 16n + lane%16) the 4 tokens 4*(lane/16) ...
+template <class Tag, int D> struct Frag<Tag, D, false> {
+  static constexpr int NK = D / 16;
+  static constexpr int NV = D / 16;
+  f32x4 k[NK];
+  f32x4 v[NV];
+  template <int Pol = kKvCachePolicy>
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
+    const int kr = (lane & 15) * (D * 4) + (lane >> 4) * 16;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) k[j] = __builtin_bit_cast(f32x4, buf_load16<Pol>(rk, kr + j * 64));
+    const int vr = (lane >> 4) * (D * 16) + (lane & 15) * 16;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) v[n] = __builtin_bit_cast(f32x4, buf_load16<Pol>(rv, vr + n * 256));
+  }
+};
+
+// Query fragment: the B operand of S = K q^T for head (lane % 16) of the group.
+template <class Tag, int D, bool H = Is16<Tag>::value> struct QFrag;
+template <class Tag, int D> struct QFrag<Tag, D, true> {
+  u32x4 q[D / 32];
+  __device__ inline void load(const char* qrow, bool valid, int lane) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const int dim0 = 8 * (4 * m + (lane >> 4));
+      q[m] = valid ? *reinterpret_cast<const u32x4*>(qrow + dim0 * 2) : u32x4{0, 0, 0, 0};
+    }
+  }
+};
+template <class Tag, int D> struct QFrag<Tag, D, false> {
+  f32x4 q[D / 16];
+  __device__ inline void load(const char* qrow, bool valid, int lane) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      const int dim0 = 4 * (4 * j + (lane >> 4));
+      q[j] = valid ? *reinterpret_cast<const f32x4*>(qrow + dim0 * 4) : f32x4{0, 0, 0, 0};
+    }
+  }
+};
+
+// Running softmax state of one wavefront: lane (h + 16 q) owns head h;
+// acc[n][r] is output dim 16n + 4q + r of that head (the MFMA C layout).
+template <int D> struct State {
+  float m;      // running max (log2 domain), identical across the head's lanes
+  float l;      // this lane's share of the running sum
+  f32x4 acc[D / 16];
+};
+
+// One sub-tile: S = K q^T, online-softmax update of (m, l), acc += V^T P.
+// n_valid: stored tokens in the sub-tile (rows past it may hold anything).
+// Causal: a column may see none of the sub-tile's rows while its state is
+// still empty (m = -inf); the exponent base then falls back to 0 so that
+// -inf - -inf never occurs.
+template <class Tag, int D, bool Causal = false>
+__device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& qf, State<D>& st,
+                                    int n_valid, float qk_scale, int lane, int lim = kRows) {
+  // 1) scores S[t][h]: lane (h + 16q) gets tokens 4q..4q+3 of head h.
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (Is16<Tag>::value) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) s = mma32<Tag>(f.k[m], qf.q[m], s);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mma4(f.k[j][e], qf.q[j][e], s);
+  }
+  const int t0 = 4 * (lane >> 4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] *= qk_scale;
+    // select, never multiply: tails may hold NaN.  `lim` (per lane: its
+    // column's last visible row + 1) is the causal limit of multi-token queries.
+    if (t0 + r >= n_valid || t0 + r >= lim) s[r] = -INFINITY;
+  }
+  // 2) online softmax.
+  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  bm = xor_max(bm);
+  const float m_new = fmaxf(st.m, bm);
+  const float m_base = (Causal && m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_base);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - m_base);
+  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  st.m = m_new;
+  // 3) acc[d][h] = alpha * acc + V^T P.
+  if constexpr (Is16<Tag>::value) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = narrow16<Tag>(p[r]);
+      lo[r] = narrow16<Tag>(p[r] - widen16<Tag>(hi[r]));
+    }
+    const u32x4 pb = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                      lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    // Tail tokens of V are zeroed (their P is zero, but 0 * NaN is NaN).
+    uint32_t keep0 = 0xffffffffu, keep1 = 0xffffffffu;
+    if (n_valid < kRows) {
+      keep0 = (t0 + 0 < n_valid ? 0x0000ffffu : 0u) | (t0 + 1 < n_valid ? 0xffff0000u : 0u);
+      keep1 = (t0 + 2 < n_valid ? 0x0000ffffu : 0u) | (t0 + 3 < n_valid ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const uint32_t a0 = f.v[n][0] & keep0, a1 = f.v[n][1] & keep1;
+      const u32x4 va = {a0, a1, a0, a1};
+      st.acc[n] *= alpha;
+      st.acc[n] = mma32<Tag>(va, pb, st.acc[n]);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      f32x4 va = f.v[n];
+      if (n_valid < kRows) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) va[e] = (t0 + e < n_valid) ? va[e] : 0.f;
+      }
+      st.acc[n] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.acc[n] = mma4(va[e], p[e], st.acc[n]);
+    }
+  }
+}
+
+template <class OutT> __device__ inline void store_out(OutT* o, float x);
+template <> __device__ inline void store_out<float>(float* o, float x) { *o = x; }
+template <> __device__ inline void store_out<__bf16>(__bf16* o, float x) { *o = static_cast<__bf16>(x); }
+template <> __device__ inline void store_out<_Float16>(_Float16* o, float x) { *o = static_cast<_Float16>(x); }
+
+template <class Tag> struct Elt { using T = uint16_t; static constexpr int bytes = 2; };
+template <> struct Elt<TagF32> { using T = float; static constexpr int bytes = 4; };
+
+
+}  // namespace pa

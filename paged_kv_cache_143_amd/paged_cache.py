@@ -217,3 +217,50 @@ class DecodeStep:
             self.write_current()
             self.attend()
         return self.out
+
+
+class PrefillStep:
+    """One multi-token step over a batch built from a chunked workload: write
+    every chunk's K/V (pa_slot_mapping + pa_write_kv), then pa_prefill_attention."""
+
+    def __init__(self, batch: Batch, out_dtype=torch.float32):
+        self.b = batch
+        w = batch.w
+        if w.chunk_lens is None:
+            raise ValueError("workload has no chunks")
+        dev = batch.q.device
+        lens = batch.bm.length_array(w.seq_names).astype(np.int64)
+        chunk = np.asarray(w.chunk_lens, dtype=np.int64)
+        starts = np.concatenate([[0], np.cumsum(chunk)])
+        self.max_chunk = int(chunk.max()) if len(chunk) else 0
+        self.q = w.chunk_queries().to(dev)
+        self.q_start = torch.from_numpy(starts.astype(np.int32)).to(dev)
+        seq = np.repeat(np.arange(w.num_seqs), chunk)
+        pos = np.concatenate([np.arange(L - n, L) for L, n in zip(lens, chunk)]) if len(chunk) \
+            else np.zeros(0, dtype=np.int64)
+        self.seq_ids = torch.from_numpy(seq.astype(np.int32)).to(dev)
+        self.positions = torch.from_numpy(pos.astype(np.int32)).to(dev)
+        self.slots = torch.empty(len(pos), dtype=torch.int32, device=dev)
+        ks, vs = [], []
+        for name, L, n in zip(w.seq_names, lens, chunk):     # chunk rows: payload key = name
+            k, v = w.kv(name)
+            ks.append(k[L - n:L])
+            vs.append(v[L - n:L])
+        self.k_new = torch.cat(ks).to(dev)
+        self.v_new = torch.cat(vs).to(dev)
+        self.out = torch.empty(self.q.shape, dtype=out_dtype, device=dev)
+
+    def write_chunks(self) -> None:
+        B.slot_mapping_t(self.b.tables, self.seq_ids, self.positions, self.slots,
+                         self.b.kv.block_size)
+        self.b.kv.write(self.k_new, self.v_new, self.slots)
+
+    def attend(self) -> None:
+        b = self.b
+        B.prefill_attention_t(b.kv.desc, b.kv.k, b.kv.v, self.q, self.out, self.q_start,
+                              b.tables, b.lens, b.w.scale, self.max_chunk, b.max_len)
+
+    def __call__(self) -> torch.Tensor:
+        self.write_chunks()
+        self.attend()
+        return self.out

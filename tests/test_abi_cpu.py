@@ -134,3 +134,26 @@ def test_validate_argument_checks():
     d = _desc()
     assert B.pa_validate_tables(d, 16, 4, 16, 2, 64, 0, 0) == B.PA_ERR_INVALID_ARG
     assert B.pa_validate_tables(d, 16, 4, 0, 2, 64, 16, 0) == B.PA_ERR_INVALID_ARG
+
+
+def test_prefill_argument_checks():
+    d = _desc()
+    base = dict(k_pool=16, v_pool=16, q=16, out=16, out_dtype=B.PA_F32, q_start=16,
+                block_tables=16, max_blocks_per_seq=4, context_lens=16, num_seqs=2,
+                num_q_heads=32, scale=0.1, max_chunk_len=40, max_context_len=64, stream=0)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return B.pa_prefill_attention(d, **a)
+
+    assert call(num_q_heads=30) == B.PA_ERR_INVALID_ARG          # not a multiple of Hkv
+    assert call(num_q_heads=8 * 17) == B.PA_ERR_UNSUPPORTED       # group of 17
+    assert call(out_dtype=B.PA_F16) == B.PA_ERR_UNSUPPORTED
+    assert call(q_start=0) == B.PA_ERR_INVALID_ARG
+    assert call(out=24) == B.PA_ERR_INVALID_ARG                   # misaligned
+    assert call(max_chunk_len=-1) == B.PA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == B.PA_ERR_INVALID_ARG
+    assert call(max_chunk_len=0) == B.PA_OK                       # nothing to do
+    assert call(num_seqs=0) == B.PA_OK
+    assert B.pa_prefill_attention(_desc(head_dim=96), **base) == B.PA_ERR_UNSUPPORTED

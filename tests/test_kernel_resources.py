@@ -28,7 +28,7 @@ def _kernels(path, tmp_path):
     return ks, text
 
 
-@pytest.mark.parametrize("src", ["pa_decode.hip", "pa_cache.hip"])
+@pytest.mark.parametrize("src", ["pa_decode.hip", "pa_cache.hip", "pa_prefill.hip"])
 def test_no_scratch_and_vgpr_budget(src, tmp_path):
     ks, text = _kernels(os.path.join(B.CSRC, src), tmp_path)
     assert ks
