@@ -21,6 +21,22 @@ behaviour restated here:
     occurrences, the free list has no duplicates and equals the zero-count
     set, every non-last block of a table is full and the last one holds
     1..b tokens.
+Swapping (transcript, paragraph 5: when the pool is empty a whole sequence
+is evicted, its K/V moved to CPU memory and restored later; "Inside vLLM and
+TGI", section "Read the vLLM0.11.0 scheduler": host swap costs the cache
+bytes in both directions):
+  * swap_out: every block of the table is copied to a fresh HOST block (host
+    blocks come from their own free list, taken at its end), then the table
+    is released as by `release`; fails with MemoryError before any change
+    when too few host blocks are free;
+  * swap_in: every host block of the sequence is copied into a fresh device
+    block (atomic: MemoryError before any change when too few are free), the
+    host blocks return to the end of the host free list in table order, and
+    the sequence is live again with its old length.
+Reading (the pages are silent): each sequence is swapped on its own; a block
+it shared with another live sequence is copied out for it, and after swap-in
+it holds private copies (sharing is not restored).
+
 The page's own model stores token ids; this one stores opaque payload
 references (whatever the caller passes), and additionally records the device
 side effects each operation implies -- token writes by flat slot and
@@ -35,12 +51,13 @@ from __future__ import annotations
 from collections import Counter
 from typing import Any, Dict, List, Optional, Sequence, Tuple
 
-Event = Tuple[str, int, Any]      # ("write", slot, payload) | ("copy", src, dst)
+# ("write", slot, payload) | ("copy", src, dst) | ("swap_out", dev, host) | ("swap_in", host, dev)
+Event = Tuple[str, int, Any]
 
 
 class BlockModel:
     def __init__(self, count: int, width: int, free_order: Optional[Sequence[int]] = None,
-                 checked: bool = True):
+                 checked: bool = True, host_count: int = 0):
         if not isinstance(count, int) or not isinstance(width, int) or count < 1 or width < 1:
             raise ValueError("pool size and block width must be positive integers")
         self.width = width
@@ -55,6 +72,10 @@ class BlockModel:
         self.tables: Dict[Any, List[int]] = {}
         self.events: List[Event] = []
         self.checked = checked
+        self.host_count = host_count
+        self.host_contents: List[List[Any]] = [[] for _ in range(host_count)]
+        self.host_free: List[int] = list(range(host_count))
+        self.swapped: Dict[Any, List[int]] = {}          # name -> host blocks, in table order
 
     # -- block ownership ---------------------------------------------------
     def _fresh_block(self) -> int:
@@ -126,6 +147,48 @@ class BlockModel:
             self._unref(blk)
         self._verify()
 
+    def swap_out(self, name: Any) -> List[Tuple[int, int]]:
+        """Move a live sequence to host blocks; returns its (device, host) copies."""
+        table = self.tables[name]
+        if len(table) > len(self.host_free):
+            raise MemoryError("host swap space full")
+        pairs = []
+        host_table = []
+        for blk in table:
+            hb = self.host_free.pop()
+            self.host_contents[hb] = list(self.contents[blk])
+            self.events.append(("swap_out", blk, hb))
+            pairs.append((blk, hb))
+            host_table.append(hb)
+        for blk in self.tables.pop(name):
+            self._unref(blk)
+        self.swapped[name] = host_table
+        self._verify()
+        return pairs
+
+    def swap_in(self, name: Any) -> List[Tuple[int, int]]:
+        """Bring a swapped sequence back into fresh device blocks; returns its
+        (host, device) copies."""
+        host_table = self.swapped[name]
+        if name in self.tables:
+            raise ValueError("name already live")
+        if len(host_table) > len(self.free):
+            raise MemoryError("pool full")
+        table, pairs = [], []
+        for hb in host_table:
+            blk = self._fresh_block()
+            self.contents[blk] = list(self.host_contents[hb])
+            self.events.append(("swap_in", hb, blk))
+            pairs.append((hb, blk))
+            table.append(blk)
+        for hb in host_table:
+            self.host_contents[hb] = []
+            self.host_free.append(hb)
+        del self.swapped[name]
+        self.tables[name] = table
+        self._verify()
+        return pairs
+
     # -- views ---------------------------------------------------------------
     def read(self, name: Any) -> List[Any]:
         """Payloads of a table in logical order (walks the table)."""
@@ -148,14 +211,18 @@ class BlockModel:
         for table in self.tables.values():
             assert all(len(self.contents[blk]) == self.width for blk in table[:-1]), "gap"
             assert 1 <= len(self.contents[table[-1]]) <= self.width, "last block fill"
+        held = [hb for t in self.swapped.values() for hb in t]
+        assert len(set(self.host_free)) == len(self.host_free), "duplicate host free id"
+        assert sorted(held + self.host_free) == list(range(self.host_count)), "host blocks"
+        assert not set(self.swapped) & set(self.tables), "swapped and live"
 
 
 def run_script(ops, num_blocks: int, width: int, free_order: Sequence[int],
-               checked: bool = True) -> BlockModel:
-    """Replay an op script.  Each op has .kind in {create, fork, append, release},
-    .name, and for create .count/.key (payload rows (key, 0..count-1)), for fork
-    .src, for append .key/.index (payload (key, index))."""
-    model = BlockModel(num_blocks, width, free_order, checked=checked)
+               checked: bool = True, host_blocks: int = 0) -> BlockModel:
+    """Replay an op script.  Each op has .kind in {create, fork, append, release,
+    swap_out, swap_in}, .name, and for create .count/.key (payload rows
+    (key, 0..count-1)), for fork .src, for append .key/.index (payload (key, index))."""
+    model = BlockModel(num_blocks, width, free_order, checked=checked, host_count=host_blocks)
     for op in ops:
         if op.kind == "create":
             model.create(op.name, [(op.key, r) for r in range(op.count)])
@@ -165,6 +232,10 @@ def run_script(ops, num_blocks: int, width: int, free_order: Sequence[int],
             model.append(op.name, (op.key, op.index))
         elif op.kind == "release":
             model.release(op.name)
+        elif op.kind == "swap_out":
+            model.swap_out(op.name)
+        elif op.kind == "swap_in":
+            model.swap_in(op.name)
         else:
             raise ValueError(op.kind)
     return model

@@ -11,6 +11,10 @@ it, mirroring the device side effects of the allocator:
   write(slot, payload)   one token's K and V rows for every KV head
   copy(src, dst)         every slot of block src into block dst (all b slots,
                          written or not)
+and two move whole blocks to and from a host pool of the same shape
+(swapping, transcript paragraph 5):
+  swap_out(dev, host)    every slot of device block dev into host block host
+  swap_in(host, dev)     every slot of host block host into device block dev
 Values are resolved only when asked, in fp64, in the layout
 [block][offset][kv head][dim] -- deliberately not the device layout.
 """
@@ -22,10 +26,12 @@ import numpy as np
 
 
 class SlotPool:
-    def __init__(self, num_blocks: int, width: int):
+    def __init__(self, num_blocks: int, width: int, host_blocks: int = 0):
         self.num_blocks = num_blocks
         self.width = width
         self.slots: List[Optional[Any]] = [None] * (num_blocks * width)
+        self.host_blocks = host_blocks
+        self.host: List[Optional[Any]] = [None] * (host_blocks * width)
 
     def write(self, slot: int, payload: Any) -> None:
         if slot < 0:
@@ -36,14 +42,30 @@ class SlotPool:
         b = self.width
         self.slots[dst * b:(dst + 1) * b] = self.slots[src * b:(src + 1) * b]
 
+    def swap_out(self, dev: int, host: int) -> None:
+        b = self.width
+        self.host[host * b:(host + 1) * b] = self.slots[dev * b:(dev + 1) * b]
+
+    def swap_in(self, host: int, dev: int) -> None:
+        b = self.width
+        self.slots[dev * b:(dev + 1) * b] = self.host[host * b:(host + 1) * b]
+
     def replay(self, events: Iterable[Tuple[str, int, Any]]) -> None:
         for kind, a, c in events:
             if kind == "write":
                 self.write(a, c)
             elif kind == "copy":
                 self.copy(a, c)
+            elif kind == "swap_out":
+                self.swap_out(a, c)
+            elif kind == "swap_in":
+                self.swap_in(a, c)
             else:
                 raise ValueError(kind)
+
+    def host_block_payloads(self, hb: int) -> List[Optional[Any]]:
+        b = self.width
+        return self.host[hb * b:(hb + 1) * b]
 
     def block_payloads(self, blk: int) -> List[Optional[Any]]:
         b = self.width

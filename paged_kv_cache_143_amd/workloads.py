@@ -37,6 +37,7 @@ DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 # Op kinds of an allocator script.
 CREATE, FORK, APPEND, RELEASE = "create", "fork", "append", "release"
+SWAP_OUT, SWAP_IN = "swap_out", "swap_in"
 
 
 def _mix(*parts: int) -> int:
@@ -68,6 +69,7 @@ class Op:
     fork:    name becomes a sharer of every block of `src`
     append:  name grows by one token whose payload row is data[key][index]
     release: name is dropped
+    swap_out / swap_in: name moves to host blocks / back to device blocks
     """
     kind: str
     name: int
@@ -97,6 +99,7 @@ class Workload:
     # Multi-token workloads: the chunk of sequence i is its chunk_lens[i]
     # newest tokens (payload rows L-n .. L-1 of key i); None for decode.
     chunk_lens: Optional[List[int]] = None
+    host_blocks: int = 0            # host swap space, in blocks
     _cache: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = field(default_factory=dict, repr=False)
 
     @property
@@ -238,6 +241,7 @@ def fork_payload_rows(w: Workload) -> Dict[int, List[Tuple[int, int]]]:
     to contain), used by tests as the un-paged "contiguous" view.
     """
     seqs: Dict[int, List[Tuple[int, int]]] = {}
+    parked: Dict[int, List[Tuple[int, int]]] = {}          # swapped out
     for op in w.ops:
         if op.kind == CREATE:
             seqs[op.name] = [(op.key, r) for r in range(op.count)]
@@ -247,6 +251,10 @@ def fork_payload_rows(w: Workload) -> Dict[int, List[Tuple[int, int]]]:
             seqs[op.name].append((op.key, op.index))
         elif op.kind == RELEASE:
             del seqs[op.name]
+        elif op.kind == SWAP_OUT:
+            parked[op.name] = seqs.pop(op.name)
+        elif op.kind == SWAP_IN:
+            seqs[op.name] = parked.pop(op.name)
     return seqs
 
 

@@ -18,8 +18,8 @@ class OracleRun:
     def __init__(self, w, checked: bool = False):
         self.w = w
         self.model: BlockModel = run_script(w.ops, w.num_blocks, w.block_size, w.free_order,
-                                            checked=checked)
-        self.pool = SlotPool(w.num_blocks, w.block_size)
+                                            checked=checked, host_blocks=w.host_blocks)
+        self.pool = SlotPool(w.num_blocks, w.block_size, w.host_blocks)
         self.pool.replay(self.model.events)
         self._f64: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
 
