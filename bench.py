@@ -37,6 +37,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "decode_step_gqa_bf16_b256_counters.js
 KERNEL_SOURCES = ("paged_kv_cache_143_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_143_amd/csrc/pa_tile.h",
                   "paged_kv_cache_143_amd/csrc/pa_internal.h")
+PCIE_PEAK_GBS = 64.0            # host link: PCIe 5.0 x16, one direction, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense, published
 
 
@@ -58,6 +59,8 @@ def _workloads():
         "gqa-bf16-b256-bs32": (lambda: W.gqa_bf16_block(32), 0,
                                "uniform int 200..2000, 32-token blocks"),
         "tiny-f32": (W.tiny_f32, 0, "{50, 20, 65, 16}"),
+        "swap-gqa-bf16": (W.swap_gqa_bf16, 0,
+                          "uniform int 200..2000; every third sequence swapped out and back"),
         "prefill-bf16": (W.prefill_bf16, 0, "16 prompts x 2048 tokens, no cached prefix"),
         "chunked-prefill-bf16": (W.chunked_prefill_bf16, 0,
                                  "32 x 512-token chunks over cached prefixes U{512..4096}"),
@@ -297,6 +300,92 @@ def run_prefill(args, w, length_desc):
     print(json.dumps(line), flush=True)
 
 
+def run_swap(args, w, length_desc):
+    """Swap every block of the workload's swapped sequences out to pinned host
+    memory and back (pa_swap_blocks both ways), and the pages' cost check: the
+    swap time against recomputing those sequences' attention by prefill."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_143_amd import binding as B
+    from paged_kv_cache_143_amd import workloads as W
+    from paged_kv_cache_143_amd.paged_cache import PrefillStep, build_batch
+
+    batch = build_batch(w, device="cuda")
+    names = sorted({op.name for op in w.ops if op.kind == W.SWAP_OUT})
+    dev_blocks = [blk for n in names for blk in batch.bm.tables[n]]
+    nb = len(dev_blocks)
+    if nb > w.host_blocks:
+        raise RuntimeError("host swap space smaller than the swapped sequences")
+    out_pairs = torch.tensor([[d, h] for h, d in enumerate(dev_blocks)], dtype=torch.int32,
+                             device="cuda")
+    in_pairs = out_pairs.flip(1).contiguous()
+    kv = batch.kv
+    block_bytes = w.num_kv_heads * w.block_size * w.head_dim * (2 if w.dtype != "f32" else 4)
+    moved = nb * 2 * block_bytes                      # K and V, one direction
+    for _ in range(args.warmup):
+        kv.swap(out_pairs, B.PA_SWAP_OUT)
+        kv.swap(in_pairs, B.PA_SWAP_IN)
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(mk(), mk(), mk()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b_, c in ev:
+        a.record()
+        kv.swap(out_pairs, B.PA_SWAP_OUT)
+        b_.record()
+        kv.swap(in_pairs, B.PA_SWAP_IN)
+        c.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_out = np.array([a.elapsed_time(b_) for a, b_, _ in ev])
+    t_in = np.array([b_.elapsed_time(c) for _, b_, c in ev])
+    ms_step = wall / args.steps * 1e3
+    gbs_out = moved / (np.median(t_out) / 1e3) / 1e9
+    gbs_in = moved / (np.median(t_in) / 1e3) / 1e9
+    # recompute alternative: prefill attention over the same sequences (attention only)
+    lens = [int(batch.bm.lengths[n]) for n in names]
+    pw = W.chunked("recompute", 9, w.dtype, [0] * len(lens), lens, w.num_q_heads,
+                   w.num_kv_heads, w.head_dim, block_size=w.block_size)
+    pstep = PrefillStep(build_batch(pw, device="cuda"))
+    pstep.attend()
+    torch.cuda.synchronize()
+    pe = [(mk(), mk()) for _ in range(5)]
+    for a, b_ in pe:
+        a.record()
+        pstep.attend()
+        b_.record()
+    torch.cuda.synchronize()
+    t_rec = float(np.median([a.elapsed_time(b_) for a, b_ in pe]))
+    t_swap = float(np.median(t_out) + np.median(t_in))
+    line = {
+        "metric": "KV swap GB/s (device->host + host->device, pinned host pools), 1 GPU",
+        "value": round(2 * moved / (t_swap / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "lengths": length_desc,
+                   "swapped_sequences": len(names), "blocks": nb,
+                   "bytes_each_way": moved, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "step": "pa_swap_blocks out + pa_swap_blocks in"},
+        "kernels_us": {"swap_out_median": round(float(np.median(t_out)) * 1e3, 1),
+                       "swap_in_median": round(float(np.median(t_in)) * 1e3, 1)},
+        "swap_out_gbs": round(gbs_out, 2), "swap_in_gbs": round(gbs_in, 2),
+        "cost_check": {"t_swap_ms": round(t_swap, 3),
+                       "t_swap_formula_ms": round(2 * moved / (min(gbs_out, gbs_in) * 1e9) * 1e3, 3),
+                       "t_recompute_attention_only_ms": round(t_rec, 3),
+                       "note": "recompute would also redo every layer's projections and MLP "
+                               "for these tokens; only the attention part is timed here"},
+        "roofline": {"bound": "link", "achieved": round(min(gbs_out, gbs_in), 2),
+                     "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(min(gbs_out, gbs_in) / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_swap_blocks (swap_blocks_kernel)"},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run(args):
     import numpy as np
     import torch
@@ -321,6 +410,8 @@ def run(args):
     w = make()
     if w.chunk_lens is not None:
         return run_prefill(args, w, length_desc)
+    if w.host_blocks > 0:
+        return run_swap(args, w, length_desc)
     if args.partition is None:
         args.partition = default_ps
     t_setup = time.perf_counter()

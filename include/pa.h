@@ -268,6 +268,35 @@ PA_API pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_po
                                       int32_t num_q_heads, float scale, int32_t max_chunk_len,
                                       int32_t max_context_len, void* stream);
 
+/* Directions of pa_swap_blocks. */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+
+/*
+ * pa_swap_blocks -- preemption by swapping: copy whole blocks (every slot,
+ * both pools, all KV heads) between the device pools and host pools of the
+ * same layout.  When the pool is exhausted a whole sequence is evicted and
+ * its K/V moved to CPU memory, to be restored later (transcript, paragraph
+ * 5); the cost is the cache bytes in each direction ("Inside vLLM and TGI",
+ * section "Read the vLLM0.11.0 scheduler").
+ *   host_k, host_v    HOST, page-locked (hipHostMalloc or an equivalent pinned
+ *                     allocation) and mapped for the current device: host
+ *                     block hb starts at byte hb * Hkv * b * head_dim * s; the
+ *                     GPU reads or writes them directly (no staging copy)
+ *   host_num_blocks   blocks in each host pool
+ *   block_pairs       device int32 [n_pairs][2] (src, dst): for PA_SWAP_OUT
+ *                     (device block, host block), for PA_SWAP_IN (host block,
+ *                     device block); a pair with an id out of range is skipped;
+ *                     no block may be the destination of two pairs
+ *   direction         PA_SWAP_OUT or PA_SWAP_IN
+ * Host pools that are not pinned host memory are rejected (PA_ERR_INVALID_ARG)
+ * before anything is enqueued.  The host data is complete once the stream has
+ * passed the call.
+ */
+PA_API pa_status pa_swap_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                                void* host_k, void* host_v, int32_t host_num_blocks,
+                                const int32_t* block_pairs, int32_t n_pairs, int32_t direction,
+                                void* stream);
+
 /*
  * pa_validate_tables -- debug check of device-resident tables before a
  * kernel consumes them ("Inside vLLM and TGI", section "Exact CPU block

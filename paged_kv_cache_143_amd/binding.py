@@ -22,7 +22,8 @@ DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_attention",
-           "pa_decode_step", "pa_prefill_attention", "pa_validate_tables")
+           "pa_decode_step", "pa_prefill_attention", "pa_swap_blocks", "pa_validate_tables")
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 
 
 class PaError(RuntimeError):
@@ -88,6 +89,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_prefill_attention.restype = I32
     L.pa_prefill_attention.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I32, P, P, I32, P,
                                        I32, I32, ctypes.c_float, I32, I32, P]
+    L.pa_swap_blocks.restype = I32
+    L.pa_swap_blocks.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I32, P, I32, I32, P]
     L.pa_validate_tables.restype = I32
     L.pa_validate_tables.argtypes = [ctypes.POINTER(PoolDesc), P, I32, P, I32, I32, P, P]
     return L
@@ -161,6 +164,12 @@ def pa_prefill_attention(desc, k_pool, v_pool, q, out, out_dtype, q_start, block
                                       q_start, block_tables, max_blocks_per_seq, context_lens,
                                       num_seqs, num_q_heads, scale, max_chunk_len,
                                       max_context_len, stream)
+
+
+def pa_swap_blocks(desc, k_pool, v_pool, host_k, host_v, host_num_blocks, block_pairs, n_pairs,
+                   direction, stream) -> int:
+    return lib().pa_swap_blocks(ctypes.byref(desc), k_pool, v_pool, host_k, host_v,
+                                host_num_blocks, block_pairs, n_pairs, direction, stream)
 
 
 def pa_validate_tables(desc, block_tables, max_blocks_per_seq, context_lens, num_seqs,
@@ -287,6 +296,19 @@ def prefill_attention_t(desc, k_pool, v_pool, q, out, q_start, block_tables, con
                                 _ptr(q_start), _ptr(block_tables), M, _ptr(context_lens), S,
                                 q.shape[1], float(scale), int(max_chunk_len),
                                 int(max_context_len), _stream()))
+
+
+def swap_blocks_t(desc, k_pool, v_pool, host_k, host_v, host_num_blocks, pairs,
+                  direction) -> None:
+    _dev_i32(pairs, "pairs")
+    if host_k.is_cuda or host_v.is_cuda or not host_k.is_pinned() or not host_v.is_pinned():
+        raise ValueError("host pools must be pinned host tensors")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n][2]")
+    _check("pa_swap_blocks",
+           pa_swap_blocks(desc, _ptr(k_pool), _ptr(v_pool), host_k.data_ptr(), host_v.data_ptr(),
+                          int(host_num_blocks), _ptr(pairs), pairs.shape[0], int(direction),
+                          _stream()))
 
 
 def validate_tables_t(desc, block_tables, context_lens, max_context_len, bad_count) -> None:

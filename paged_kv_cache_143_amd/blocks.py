@@ -10,11 +10,15 @@ Operations", section "Exact CPU block manager and copy-on-write", and the
   * forks share every block (reference counts); appending to a shared,
     partially filled last block first copies it to a fresh block;
   * admission and growth fail with MemoryError before any change when no
-    block is free.
+    block is free;
+  * swapping (transcript, paragraph 5): a live sequence moves to host blocks
+    (its own free list, taken at the end) and its device blocks are released;
+    swapping in takes fresh device blocks for every host block and returns the
+    host blocks in table order; both fail before any change without space.
 The manager keeps only counts (token contents live in the device pool) and
 reports the device work each operation implies: token writes by slot and
 block copies, which `paged_cache.PagedKV` turns into pa_write_kv and
-pa_copy_blocks calls.
+pa_copy_blocks calls, and (device, host) block pairs for pa_swap_blocks.
 """
 from __future__ import annotations
 
@@ -25,7 +29,7 @@ import numpy as np
 
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int = 16,
-                 free_order: Optional[Sequence[int]] = None):
+                 free_order: Optional[Sequence[int]] = None, host_blocks: int = 0):
         if num_blocks < 1 or block_size < 1:
             raise ValueError("num_blocks and block_size must be positive")
         self.num_blocks = num_blocks
@@ -38,6 +42,9 @@ class BlockManager:
         self.free: List[int] = order
         self.tables: Dict[Hashable, List[int]] = {}
         self.lengths: Dict[Hashable, int] = {}
+        self.host_blocks = host_blocks
+        self.host_free: List[int] = list(range(host_blocks))
+        self.swapped: Dict[Hashable, List[int]] = {}
 
     # -- helpers ------------------------------------------------------------
     def _take(self) -> int:
@@ -104,6 +111,31 @@ class BlockManager:
             self._drop(blk)
         del self.lengths[name]
 
+    def swap_out(self, name: Hashable) -> List[Tuple[int, int]]:
+        """Evict a live sequence to host blocks; returns the (device, host) block
+        pairs to copy before the device blocks are reused."""
+        table = self.tables[name]
+        if len(table) > len(self.host_free):
+            raise MemoryError("host swap space full")
+        host = [self.host_free.pop() for _ in table]
+        for blk in self.tables.pop(name):
+            self._drop(blk)
+        self.swapped[name] = host
+        return list(zip(table, host))
+
+    def swap_in(self, name: Hashable) -> List[Tuple[int, int]]:
+        """Restore a swapped sequence; returns the (host, device) block pairs to copy."""
+        host = self.swapped[name]
+        if name in self.tables:
+            raise ValueError("duplicate name")
+        if len(host) > len(self.free):
+            raise MemoryError("pool full")
+        table = [self._take() for _ in host]
+        self.host_free.extend(host)
+        del self.swapped[name]
+        self.tables[name] = table
+        return list(zip(host, table))
+
     # -- device views ---------------------------------------------------------
     def table_array(self, names: Sequence[Hashable], width: Optional[int] = None,
                     pad: int = 0x7FFFFFFF) -> np.ndarray:
@@ -130,4 +162,8 @@ class BlockManager:
         assert len(set(self.free)) == len(self.free)
         assert set(self.free) == set(np.nonzero(self.refs == 0)[0].tolist())
         for name, t in self.tables.items():
+            assert len(t) == (self.lengths[name] + self.b - 1) // self.b
+        held = [hb for t in self.swapped.values() for hb in t]
+        assert sorted(held + self.host_free) == list(range(self.host_blocks))
+        for name, t in self.swapped.items():
             assert len(t) == (self.lengths[name] + self.b - 1) // self.b

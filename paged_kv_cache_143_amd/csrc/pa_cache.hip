@@ -100,6 +100,67 @@ __global__ void copy_blocks_kernel(char* __restrict__ k_pool, char* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Swap: whole blocks between the device pools and pinned host pools of the
+// same layout (preemption by swapping; the K/V of an evicted sequence is
+// moved to CPU memory and restored later).  A workgroup moves one 16 KiB
+// segment of one block of one pool: wavefront w, lane l handles 16-byte
+// vectors seg*1024 + 256w + 64j + l, j = 0..3, all four loads issued before
+// the stores, so each instruction covers 1 KiB contiguous and a host read
+// keeps four requests in flight per lane.
+// ---------------------------------------------------------------------------
+constexpr int kSwapSegVecs = 1024;
+
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const char* __restrict__ src_k, const char* __restrict__ src_v, char* __restrict__ dst_k,
+    char* __restrict__ dst_v, const int32_t* __restrict__ pairs, int32_t n_pairs,
+    int64_t block_vecs, int32_t segs, int32_t src_blocks, int32_t dst_blocks) {
+  const int unit = blockIdx.x;
+  const int per_pair = 2 * segs;
+  const int p = unit / per_pair;
+  if (p >= n_pairs) return;
+  int r = unit - p * per_pair;
+  const bool is_v = r >= segs;
+  if (is_v) r -= segs;
+  const int32_t src = pairs[2 * p];
+  const int32_t dst = pairs[2 * p + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const u32x4* s = reinterpret_cast<const u32x4*>(is_v ? src_v : src_k) + (int64_t)src * block_vecs;
+  u32x4* d = reinterpret_cast<u32x4*>(is_v ? dst_v : dst_k) + (int64_t)dst * block_vecs;
+  const int64_t base = (int64_t)r * kSwapSegVecs + (threadIdx.x >> 6) * 256 + (threadIdx.x & 63);
+  u32x4 x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = base + 64 * j;
+    if (i < block_vecs) x[j] = s[i];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = base + 64 * j;
+    if (i < block_vecs) d[i] = x[j];
+  }
+}
+
+// Device address of a pinned host range [p, p + bytes), or null when the range
+// is not page-locked host memory mapped for the current device.
+static char* pinned_device_address(void* p, int64_t bytes) {
+  hipPointerAttribute_t first, last;
+  if (hipPointerGetAttributes(&first, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (hipPointerGetAttributes(&last, (char*)p + bytes - 1) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (first.type != hipMemoryTypeHost || last.type != hipMemoryTypeHost ||
+      !first.devicePointer || !last.devicePointer)
+    return nullptr;
+  char* d = (char*)first.devicePointer;
+  if ((char*)last.devicePointer != d + bytes - 1) return nullptr;    // one mapping
+  return d;
+}
+
+// ---------------------------------------------------------------------------
 // Validation: count lengths out of range and referenced entries out of range.
 // ---------------------------------------------------------------------------
 __global__ void zero_int_kernel(int32_t* p) { *p = 0; }
@@ -206,6 +267,36 @@ pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
   if (blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
   copy_blocks_kernel<<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
       (char*)k_pool, (char*)v_pool, block_pairs, n_pairs, block_vecs, pool->num_blocks);
+  return launch_status();
+}
+
+pa_status pa_swap_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool, void* host_k,
+                         void* host_v, int32_t host_num_blocks, const int32_t* block_pairs,
+                         int32_t n_pairs, int32_t direction, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (n_pairs < 0 || host_num_blocks < 0 ||
+      (direction != PA_SWAP_OUT && direction != PA_SWAP_IN))
+    return PA_ERR_INVALID_ARG;
+  if (n_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !host_k || !host_v || !block_pairs || host_num_blocks == 0)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(host_k) || !aligned16(host_v))
+    return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes = (int64_t)pool->num_kv_heads * tile_elems(pool) * elem_bytes(pool->dtype);
+  const int64_t host_bytes = (int64_t)host_num_blocks * block_bytes;
+  char* hk = pinned_device_address(host_k, host_bytes);
+  char* hv = pinned_device_address(host_v, host_bytes);
+  if (!hk || !hv) return PA_ERR_INVALID_ARG;
+  const int64_t block_vecs = block_bytes / 16;
+  const int64_t segs = (block_vecs + kSwapSegVecs - 1) / kSwapSegVecs;
+  const int64_t units = (int64_t)n_pairs * 2 * segs;
+  if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const bool out = direction == PA_SWAP_OUT;
+  swap_blocks_kernel<<<(unsigned)units, 256, 0, (hipStream_t)stream>>>(
+      out ? (const char*)k_pool : hk, out ? (const char*)v_pool : hv, out ? hk : (char*)k_pool,
+      out ? hv : (char*)v_pool, block_pairs, n_pairs, block_vecs, (int32_t)segs,
+      out ? pool->num_blocks : host_num_blocks, out ? host_num_blocks : pool->num_blocks);
   return launch_status();
 }
 

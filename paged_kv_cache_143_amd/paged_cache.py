@@ -20,11 +20,13 @@ import torch
 
 from . import binding as B
 from .blocks import BlockManager
-from .workloads import CREATE, FORK, APPEND, RELEASE, DTYPES, TABLE_PAD, Workload
+from .workloads import (APPEND, CREATE, DTYPES, FORK, RELEASE, SWAP_IN, SWAP_OUT, TABLE_PAD,
+                        Workload)
 
 class PagedKV:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
-                 device: str = "cuda", poison: bool = True, block_size: int = 16):
+                 device: str = "cuda", poison: bool = True, block_size: int = 16,
+                 host_blocks: int = 0):
         self.desc = B.make_desc(num_blocks, num_kv_heads, head_dim, dtype, block_size)
         self.dtype = dtype
         self.block_size = block_size
@@ -34,6 +36,14 @@ class PagedKV:
         if poison:                                   # stale/unused slots read as NaN
             self.k.fill_(float("nan"))
             self.v.fill_(float("nan"))
+        # host swap space: pinned (page-locked) memory in the same block layout
+        self.host_blocks = host_blocks
+        helems = host_blocks * num_kv_heads * block_size * head_dim
+        self.host_k = torch.empty(helems, dtype=DTYPES[dtype], pin_memory=host_blocks > 0)
+        self.host_v = torch.empty(helems, dtype=DTYPES[dtype], pin_memory=host_blocks > 0)
+        if poison:
+            self.host_k.fill_(float("nan"))
+            self.host_v.fill_(float("nan"))
 
     @property
     def num_blocks(self) -> int:
@@ -44,6 +54,11 @@ class PagedKV:
 
     def copy(self, pairs: torch.Tensor) -> None:
         B.copy_blocks_t(self.desc, self.k, self.v, pairs)
+
+    def swap(self, pairs: torch.Tensor, direction: int) -> None:
+        """(src, dst) block pairs: device -> host (B.PA_SWAP_OUT) or host -> device."""
+        B.swap_blocks_t(self.desc, self.k, self.v, self.host_k, self.host_v, self.host_blocks,
+                        pairs, direction)
 
 
 @dataclass
@@ -79,6 +94,7 @@ class _Flusher:
         self.copy_dsts = set()
         self.write_calls = 0
         self.copy_calls = 0
+        self.swap_calls = 0
 
     def add_write(self, slot: int, key: int, row: int) -> None:
         # one call must not write a slot twice (which write lands is unspecified)
@@ -89,10 +105,20 @@ class _Flusher:
         self.write_blocks.add(slot // self.kv.block_size)
 
     def add_copy(self, src: int, dst: int) -> None:
-        if src in self.write_blocks or src in self.copy_dsts:
+        # copies run before writes: flush first when the copy reads a block with
+        # pending writes or another copy's output, or overwrites a block that
+        # pending writes (an earlier tenant's) would land in afterwards
+        if src in self.write_blocks or src in self.copy_dsts or dst in self.write_blocks:
             self.flush()
         self.pairs.append((src, dst))
         self.copy_dsts.add(dst)
+
+    def swap(self, pairs: List[Tuple[int, int]], direction: int) -> None:
+        """Swaps are issued at once, in order, after everything pending."""
+        self.flush()
+        if pairs:
+            self.kv.swap(torch.tensor(pairs, dtype=torch.int32).to(self.device), direction)
+            self.swap_calls += 1
 
     def flush(self) -> None:
         if self.pairs:
@@ -126,8 +152,9 @@ class _Flusher:
 
 def build_batch(w: Workload, device: str = "cuda", poison: bool = True,
                 table_width: Optional[int] = None, drop_payload_cache: bool = True) -> Batch:
-    kv = PagedKV(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, device, poison, w.block_size)
-    bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
+    kv = PagedKV(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, device, poison, w.block_size,
+                 w.host_blocks)
+    bm = BlockManager(w.num_blocks, w.block_size, w.free_order, host_blocks=w.host_blocks)
     fl = _Flusher(w, kv, device)
     last: Dict[int, Tuple[int, int]] = {}
     copies: List[Tuple[int, int]] = []
@@ -148,6 +175,10 @@ def build_batch(w: Workload, device: str = "cuda", poison: bool = True,
             last[op.name] = (op.key, op.index)
         elif op.kind == RELEASE:
             bm.release(op.name)
+        elif op.kind == SWAP_OUT:
+            fl.swap(bm.swap_out(op.name), B.PA_SWAP_OUT)
+        elif op.kind == SWAP_IN:
+            fl.swap(bm.swap_in(op.name), B.PA_SWAP_IN)
         else:
             raise ValueError(op.kind)
     fl.flush()

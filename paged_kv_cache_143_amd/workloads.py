@@ -327,6 +327,56 @@ def chunked_prefill_bf16(num_seqs: int = 32, chunk: int = 512, seed: int = 7) ->
     return chunked("chunked-prefill-bf16", seed, "bf16", prefix, [chunk] * num_seqs, 32, 8, 128)
 
 
+def swap_cycle(name: str, seed: int, dtype: str, lengths: Sequence[int], num_q_heads: int,
+               num_kv_heads: int, head_dim: int, block_size: int = 16,
+               every: int = 3) -> Workload:
+    """Preemption by swapping: every `every`-th sequence is swapped out after
+    its prompt, other requests (fillers) then occupy the freed blocks while the
+    rest decode one token, the fillers finish, and the swapped sequences come
+    back (into other blocks) and decode their token.  Sequence i holds L_i
+    tokens at the end; the batch is every original sequence."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(L) for L in lengths]
+    b = block_size
+    need = sum(-(-L // b) for L in lengths)
+    num_blocks = int(need * 1.15) + 4
+    ops: List[Op] = []
+    data_len: Dict[int, int] = {}
+    for i, L in enumerate(lengths):
+        data_len[i] = L
+        ops.append(Op(CREATE, name=i, count=max(L - 1, 1), key=i))
+    out = [i for i in range(len(lengths)) if i % every == 0 and lengths[i] >= 2]
+    for i in out:
+        ops.append(Op(SWAP_OUT, name=i))
+    fillers = []
+    for k, i in enumerate(out):
+        f = 1_000_000 + k
+        data_len[f] = lengths[i]
+        ops.append(Op(CREATE, name=f, count=lengths[i], key=f))
+        fillers.append(f)
+    for i, L in enumerate(lengths):
+        if i not in out and L >= 2:
+            ops.append(Op(APPEND, name=i, key=i, index=L - 1))
+    for f in fillers:
+        ops.append(Op(RELEASE, name=f))
+    for i in out:
+        ops.append(Op(SWAP_IN, name=i))
+        ops.append(Op(APPEND, name=i, key=i, index=lengths[i] - 1))
+    host = sum(-(-lengths[i] // b) for i in out) + 2      # room for a second cycle at L
+    return Workload(name=name, seed=seed, dtype=dtype, num_blocks=num_blocks, block_size=b,
+                    num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                    ops=ops, free_order=_shuffled(rng, range(num_blocks)),
+                    seq_names=list(range(len(lengths))), data_len=data_len, host_blocks=host)
+
+
+def swap_gqa_bf16(num_seqs: int = 256, seed: int = 8) -> Workload:
+    """The batch-256 GQA shape (L ~ U{200..2000}, 32 q / 8 kv heads x 128,
+    bf16) with a third of the sequences swapped out and back."""
+    rng = np.random.default_rng(seed + 100)
+    lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
+    return swap_cycle("swap-gqa-bf16", seed, "bf16", lengths, 32, 8, 128)
+
+
 def gqa_bf16_in_order(num_seqs: int = 256, seed: int = 3) -> Workload:
     """The batch-256 GQA workload with every sequence on consecutive physical
     blocks (same lengths and values): the cost of the table indirection."""

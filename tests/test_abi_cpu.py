@@ -157,3 +157,24 @@ def test_prefill_argument_checks():
     assert call(max_chunk_len=0) == B.PA_OK                       # nothing to do
     assert call(num_seqs=0) == B.PA_OK
     assert B.pa_prefill_attention(_desc(head_dim=96), **base) == B.PA_ERR_UNSUPPORTED
+
+
+def test_swap_argument_checks():
+    d = _desc()
+    base = dict(k_pool=16, v_pool=16, host_k=16, host_v=16, host_num_blocks=4, block_pairs=16,
+                n_pairs=2, direction=B.PA_SWAP_OUT, stream=0)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return B.pa_swap_blocks(d, **a)
+
+    assert call(direction=2) == B.PA_ERR_INVALID_ARG
+    assert call(n_pairs=-1) == B.PA_ERR_INVALID_ARG
+    assert call(host_num_blocks=-1) == B.PA_ERR_INVALID_ARG
+    assert call(host_k=0) == B.PA_ERR_INVALID_ARG
+    assert call(block_pairs=0) == B.PA_ERR_INVALID_ARG
+    assert call(host_v=8) == B.PA_ERR_INVALID_ARG                # misaligned
+    assert call(host_num_blocks=0) == B.PA_ERR_INVALID_ARG
+    assert call(n_pairs=0) == B.PA_OK                             # nothing to do
+    assert B.pa_swap_blocks(_desc(head_dim=96), **base) == B.PA_ERR_UNSUPPORTED

@@ -11,8 +11,8 @@ from tests.test_oracle_allocator import _random_script
 
 
 def _replay_host(w):
-    bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
-    writes, copies = [], []
+    bm = BlockManager(w.num_blocks, w.block_size, w.free_order, host_blocks=w.host_blocks)
+    writes, copies, swaps = [], [], []
     for op in w.ops:
         if op.kind == W.CREATE:
             for r, s in enumerate(bm.create(op.name, op.count)):
@@ -24,10 +24,14 @@ def _replay_host(w):
             if cp:
                 copies.append(cp)
             writes.append((int(s), (op.key, op.index)))
+        elif op.kind == W.SWAP_OUT:
+            swaps += [("swap_out", d, h) for d, h in bm.swap_out(op.name)]
+        elif op.kind == W.SWAP_IN:
+            swaps += [("swap_in", h, d) for h, d in bm.swap_in(op.name)]
         else:
             bm.release(op.name)
         bm.check()
-    return bm, writes, copies
+    return bm, writes, copies, swaps
 
 
 @pytest.mark.parametrize("make", [W.tiny_f32, W.recycled_f32,
@@ -36,7 +40,7 @@ def _replay_host(w):
                                   lambda: W.scaled("s", 9, 20, 1, 300, 4, 2, 64, "bf16")])
 def test_host_manager_matches_oracle(make):
     w = make()
-    bm, writes, copies = _replay_host(w)
+    bm, writes, copies, swaps = _replay_host(w)
     m = run_script(w.ops, w.num_blocks, w.block_size, w.free_order, checked=False)
     assert set(bm.tables) == set(m.tables)
     for name in m.tables:
@@ -58,7 +62,7 @@ def test_random_scripts_match_oracle():
         w = W.Workload(name="r", seed=0, dtype="f32", num_blocks=pool, block_size=width,
                        num_q_heads=1, num_kv_heads=1, head_dim=1, ops=ops,
                        free_order=list(range(pool)), seq_names=[], data_len={})
-        bm, writes, copies = _replay_host(w)
+        bm, writes, copies, swaps = _replay_host(w)
         m = run_script(ops, pool, width, list(range(pool)))
         assert bm.tables == m.tables
         assert writes == [(s, p) for k, s, p in m.events if k == "write"]
@@ -96,3 +100,41 @@ def test_table_array_padding():
     assert list(arr[0, :3]) == bm.tables[0] and arr[0, 3] == W.TABLE_PAD
     assert list(arr[1, :1]) == bm.tables[1] and (arr[1, 1:] == W.TABLE_PAD).all()
     assert list(bm.length_array([0, 1])) == [40, 1]
+
+
+def test_random_swap_scripts_match_oracle():
+    from tests.test_oracle_swap import _random_swap_script
+    rng = np.random.default_rng(12)
+    for _ in range(15):
+        width = int(rng.choice([1, 4, 16]))
+        pool = int(rng.integers(4, 30))
+        host = int(rng.integers(0, 30))
+        ops = _random_swap_script(rng, 200, pool, host, width)
+        w = W.Workload(name="r", seed=0, dtype="f32", num_blocks=pool, block_size=width,
+                       num_q_heads=1, num_kv_heads=1, head_dim=1, ops=ops,
+                       free_order=list(range(pool)), seq_names=[], data_len={},
+                       host_blocks=host)
+        bm, writes, copies, swaps = _replay_host(w)
+        m = run_script(ops, pool, width, list(range(pool)), host_blocks=host)
+        assert bm.tables == m.tables and bm.swapped == m.swapped
+        assert bm.host_free == m.host_free and bm.free == m.free
+        assert writes == [(s, p) for k, s, p in m.events if k == "write"]
+        assert swaps == [e for e in m.events if e[0] in ("swap_out", "swap_in")]
+
+
+def test_swap_failures_leave_state_unchanged():
+    bm = BlockManager(4, 2, host_blocks=1)
+    bm.create("A", 3)
+    snap = (list(bm.free), bm.refs.copy(), list(bm.host_free), dict(bm.swapped))
+    with pytest.raises(MemoryError):
+        bm.swap_out("A")
+    assert snap[0] == bm.free and np.array_equal(snap[1], bm.refs)
+    assert snap[2] == bm.host_free and snap[3] == bm.swapped and "A" in bm.tables
+    bm2 = BlockManager(3, 2, host_blocks=4)
+    bm2.create("A", 3)
+    bm2.swap_out("A")
+    bm2.create("B", 4)
+    snap = (list(bm2.free), list(bm2.host_free), dict(bm2.swapped))
+    with pytest.raises(MemoryError):
+        bm2.swap_in("A")
+    assert snap == (list(bm2.free), list(bm2.host_free), dict(bm2.swapped))
