@@ -52,6 +52,7 @@ def _workloads():
         "shared-prefix-bf16-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
                                      "1016-token prompt + tails uniform 1..512"),
         "long-ctx-splitk-bf16": (W.long_ctx_bf16, -1, "uniform int 8192..32768"),
+        "gqa-fp8-b256": (W.gqa_fp8, 0, "uniform int 200..2000, FP8 E4M3 cache"),
         "gqa-bf16-b256-in-order": (W.gqa_bf16_in_order, 0,
                                    "uniform int 200..2000, consecutive physical blocks"),
         "gqa-bf16-b256-bs8": (lambda: W.gqa_bf16_block(8), 0,
@@ -92,13 +93,14 @@ def _algorithmic_bytes(w, lens, fused):
     tokens' K/V read from k_new/v_new and written to the pool."""
     import numpy as np
     L = np.asarray(lens, dtype=np.int64)
-    es = 2 if w.dtype in ("bf16", "f16") else 4
+    es = {"bf16": 2, "f16": 2, "f32": 4, "fp8": 1}[w.dtype]          # stored element
+    ies = 4 if w.dtype == "f32" else 2                                 # q, new K/V inputs
     kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * es
-    q = w.num_seqs * w.num_q_heads * w.head_dim * es
+    q = w.num_seqs * w.num_q_heads * w.head_dim * ies
     out = w.num_seqs * w.num_q_heads * w.head_dim * 4
     b = w.block_size
     tables = int(((L + b - 1) // b).sum()) * 4 + w.num_seqs * 4
-    new = 2 * (w.num_seqs * w.num_kv_heads * w.head_dim * 2 * es) if fused else 0
+    new = (w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (ies + es)) if fused else 0
     return {"kv": kv, "q": q, "out": out, "tables_lens": tables, "new_tokens": new,
             "total": kv + q + out + tables + new}
 
@@ -134,7 +136,7 @@ def cpu_baseline(w, budget_s: float):
         kk, vv = cache[p[0]]
         return kk[p[1]], vv[p[1]]
 
-    es = 4 if w.dtype == "f32" else 2
+    es = {"bf16": 2, "f16": 2, "f32": 4, "fp8": 1}[w.dtype]
     with threadpool_limits(limits=1):
         while elapsed < budget_s:
             for i in range(w.num_seqs):
@@ -320,7 +322,7 @@ def run_swap(args, w, length_desc):
                              device="cuda")
     in_pairs = out_pairs.flip(1).contiguous()
     kv = batch.kv
-    block_bytes = w.num_kv_heads * w.block_size * w.head_dim * (2 if w.dtype != "f32" else 4)
+    block_bytes = w.num_kv_heads * w.block_size * w.head_dim * {"bf16": 2, "f16": 2, "f32": 4, "fp8": 1}[w.dtype]
     moved = nb * 2 * block_bytes                      # K and V, one direction
     for _ in range(args.warmup):
         kv.swap(out_pairs, B.PA_SWAP_OUT)

@@ -63,7 +63,17 @@
  *   K; 4 consecutive tokens of one dim of V), and a token write touches
  *   2 lines of K and 8 lines of V for 128 16-bit dims.
  *
- * Supported shapes: block_size 8, 16 or 32; head_dim 64 or 128; dtype f32, f16, bf16;
+ * FP8 pools (PA_FP8_E4M3: OCP E4M3 without infinities, max 448, all-ones
+ * mantissa and exponent = NaN; one byte per element, same layout) store codes
+ * with per-KV-head scales from the descriptor.  The FP8 cache exists and its
+ * usability depends on device, backend and scales ("Inside vLLM and TGI",
+ * section "Launch a pinned engine from already reviewed local artifacts");
+ * format and scaling here are this library's choice.  Writing value x of
+ * head g stores the E4M3 value nearest to the fp32 quotient x / scale_g (ties
+ * to even), saturated to +-448; NaN stores 0x7F.  For FP8 pools the inputs
+ * k_new, v_new and q are bf16 and out_dtype is PA_F32 or PA_BF16.
+ *
+ * Supported shapes: block_size 8, 16 or 32; head_dim 64 or 128; dtype f32, f16, bf16, fp8;
  * 1 <= num_q_heads / num_kv_heads <= 16 and num_q_heads % num_kv_heads == 0.
  */
 #ifndef PA_H
@@ -89,7 +99,7 @@ enum {
 };
 
 typedef int32_t pa_dtype;
-enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 };
 
 /* partition_size value asking the library to choose (see pa_decode_attention). */
 #define PA_PARTITION_AUTO (-1)
@@ -102,6 +112,10 @@ typedef struct pa_pool_desc {
   int32_t num_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;      /* 64 or 128 */
   pa_dtype dtype;        /* element type of both pools */
+  /* PA_FP8_E4M3 pools only (NULL otherwise): device float [Hkv] per-KV-head
+   * scales; a stored K code c of head g stands for value(c) * k_scales[g]. */
+  const float* k_scales;
+  const float* v_scales;
 } pa_pool_desc;
 
 /* Human-readable name of a status; never NULL, static storage. */

@@ -16,9 +16,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpa.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_PARTITION_AUTO = -1
-DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
+DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_attention",
@@ -35,7 +35,8 @@ class PaError(RuntimeError):
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("k_scales", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -196,8 +197,11 @@ def _dev_i32(t, name):
 
 
 def make_desc(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
-              block_size: int = 16) -> PoolDesc:
-    return PoolDesc(num_blocks, block_size, num_kv_heads, head_dim, DTYPE_CODES[dtype])
+              block_size: int = 16, k_scales=None, v_scales=None) -> PoolDesc:
+    """k_scales / v_scales: device float32 tensors [Hkv] for FP8 pools (kept
+    alive by the caller), else None."""
+    return PoolDesc(num_blocks, block_size, num_kv_heads, head_dim, DTYPE_CODES[dtype],
+                    _ptr(k_scales) or None, _ptr(v_scales) or None)
 
 
 def slot_mapping_t(block_tables, seq_ids, positions, slots, block_size: int) -> None:

@@ -78,6 +78,62 @@ __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_
   }
 }
 
+// FP8 pools: bf16 inputs; a thread quantizes 16 consecutive dims of one
+// (token, head) with that head's scales into one 16-byte K store (the
+// token's row) and 16 one-byte V stores 4 bytes apart (4 tokens interleaved).
+__device__ inline uint32_t pack4_fp8(const u32x4& a, const u32x4& b, int q, float scale) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * q + j;                         // element 0..15
+    const uint32_t word = e < 8 ? a[(e & 7) >> 1] : b[(e & 7) >> 1];
+    const float x = bf16_bits_to_float((word >> ((e & 1) * 16)) & 0xFFFFu);
+    w |= fp8_code(x, scale) << (8 * j);
+  }
+  return w;
+}
+
+__global__ void write_kv_fp8_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                    const char* __restrict__ k_new, const char* __restrict__ v_new,
+                                    int64_t new_stride, const int32_t* __restrict__ slots,
+                                    int32_t n, int32_t num_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_slots,
+                                    const float* __restrict__ k_scales,
+                                    const float* __restrict__ v_scales) {
+  constexpr int X = 16;
+  const int chunks = head_dim / X;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tok = (int64_t)num_heads * chunks;
+  if (gid >= (int64_t)n * per_tok) return;
+  const int t = (int)(gid / per_tok);
+  const int rem = (int)(gid - (int64_t)t * per_tok);
+  const int h = rem / chunks;
+  const int c = rem - h * chunks;
+  const int32_t slot = slots[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int32_t blk = slot / block_size;
+  const int32_t off = slot - blk * block_size;
+  const int64_t src = ((int64_t)t * new_stride + (int64_t)h * head_dim + (int64_t)c * X) * 2;
+  const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)block_size * head_dim;  // bytes
+  const u32x4 k0 = *reinterpret_cast<const u32x4*>(k_new + src);
+  const u32x4 k1 = *reinterpret_cast<const u32x4*>(k_new + src + 16);
+  const float ks = k_scales[h];
+  u32x4 kc;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) kc[q] = pack4_fp8(k0, k1, q, ks);
+  *reinterpret_cast<u32x4*>(k_pool + tile + (int64_t)off * head_dim + (int64_t)c * X) = kc;
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(v_new + src);
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(v_new + src + 16);
+  const float vs = v_scales[h];
+  char* vb = v_pool + tile + ((int64_t)(off >> 2) * head_dim + (int64_t)c * X) * 4 + (off & 3);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = pack4_fp8(v0, v1, q, vs);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vb[(int64_t)(4 * q + j) * 4] = (char)((w >> (8 * j)) & 0xFFu);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Whole-block copies: every 16-byte vector of the (src) block in both pools.
 // ---------------------------------------------------------------------------
@@ -229,18 +285,24 @@ pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, cons
   if (n == 0) return PA_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
   const int es = elem_bytes(pool->dtype);
+  const int ies = input_bytes(pool->dtype);
   const int64_t row = (int64_t)pool->num_kv_heads * pool->head_dim;
   if (new_stride < row) return PA_ERR_INVALID_ARG;
   // 16-byte vector moves need 16-byte aligned pools, rows and token strides.
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
-      (new_stride * es) % 16 != 0)
+      (new_stride * ies) % 16 != 0)
     return PA_ERR_INVALID_ARG;
   const int64_t vecs = (int64_t)n * pool->num_kv_heads * (pool->head_dim * es / 16);
   const int threads = 256;
   const int64_t blocks = (vecs + threads - 1) / threads;
   if (blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
   const int64_t num_slots = (int64_t)pool->num_blocks * pool->block_size;
-  if (es == 2)
+  if (es == 1)
+    write_kv_fp8_kernel<<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
+        (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
+        slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots,
+        pool->k_scales, pool->v_scales);
+  else if (es == 2)
     write_kv_kernel<2><<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
         (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
         slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots);

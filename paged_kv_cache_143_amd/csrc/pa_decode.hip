@@ -76,6 +76,8 @@ struct DecodeArgs {
   int32_t num_parts;   // P = ceil(max_len / ps)
   int32_t longest_first;  // 1: map workgroups to sequences in decreasing length
   float qk_scale;      // scale * log2(e)
+  const float* k_scales;  // FP8 pools: per-KV-head scales, else null
+  const float* v_scales;
 };
 
 // Longest-first dispatch.  Workgroups start roughly in blockIdx order, so
@@ -299,6 +301,68 @@ template <class Tag, int D> struct NewToken {
 
 };
 
+// FP8 pools: the bf16 current token is quantized with its head's scales when
+// loaded; the stage holds the dequantized codes (what a read of the pool
+// returns, unscaled), and the store writes the codes -- K as one 8-byte row
+// piece per thread, V as bytes 4 apart.
+template <int D> struct NewToken<TagFP8, D> {
+  static constexpr int NC = D / 8;            // 16-byte bf16 input vectors per head row
+  uint32_t code[2];                           // the thread's 8 E4M3 codes
+
+  __device__ inline void load(const DecodeArgs& a, int seq, int g) {
+    const int t = threadIdx.x;
+    if (t < 2 * NC) {
+      const bool is_v = t >= NC;
+      const int c = is_v ? t - NC : t;
+      const char* src = (is_v ? a.v_new : a.k_new) +
+                        ((int64_t)seq * a.new_stride + (int64_t)g * D) * 2;
+      const u32x4 vec = *reinterpret_cast<const u32x4*>(src + c * 16);
+      const float scale = is_v ? a.v_scales[g] : a.k_scales[g];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * w + j;
+          const float f = bf16_bits_to_float((vec[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+          x |= fp8_code(f, scale) << (8 * j);
+        }
+        code[w] = x;
+      }
+    }
+  }
+
+  __device__ inline void stage(char* stage) const {
+    const int t = threadIdx.x;
+    if (t >= 2 * NC) return;
+    const bool is_v = t >= NC;
+    const int c = is_v ? t - NC : t;
+    const u32x4 deq = {fp8x2_to_bf16x2<false>(code[0]), fp8x2_to_bf16x2<true>(code[0]),
+                       fp8x2_to_bf16x2<false>(code[1]), fp8x2_to_bf16x2<true>(code[1])};
+    *reinterpret_cast<u32x4*>(stage + (is_v ? D * 2 : 0) + c * 16) = deq;
+  }
+
+  __device__ inline void store(const DecodeArgs& a, const int32_t* trow, int j, int g,
+                               int o) const {
+    const int64_t kTile = (int64_t)a.block_size * D;
+    const int t = threadIdx.x;
+    if (t >= 2 * NC) return;
+    const int phys = trow[j];
+    if (phys < 0 || phys >= a.num_blocks) return;
+    const bool is_v = t >= NC;
+    const int c = is_v ? t - NC : t;
+    char* tile = (is_v ? a.v_pool : a.k_pool) + ((int64_t)phys * a.num_kv_heads + g) * kTile;
+    if (!is_v) {
+      *reinterpret_cast<u32x2*>(tile + (int64_t)o * D + c * 8) = u32x2{code[0], code[1]};
+    } else {
+      char* vb = tile + (int64_t)(o >> 2) * D * 4 + (o & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vb[(int64_t)(c * 8 + e) * 4] = (char)((code[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+    }
+  }
+};
+
 // One workgroup per (KV head, sequence, partition); see the file comment.
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 3
@@ -311,9 +375,17 @@ template <class Tag, int D> struct WavesPerEU {
   static constexpr int value = (!Is16<Tag>::value && D == 128) ? 2 : PA_WAVES_PER_EU;
 };
 
+// Register buffers in the block ring: FP8 sub-tiles are half the bytes, so
+// two are kept in flight ahead of the one being computed.
+#ifndef PA_FP8_BUFS
+#define PA_FP8_BUFS 3
+#endif
+template <class Tag> struct RingBufs { static constexpr int value = IsFP8<Tag>::value ? PA_FP8_BUFS : 2; };
+
 template <class Tag, int D, class OutT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_kernel(DecodeArgs a) {
+  constexpr int NBuf = RingBufs<Tag>::value;
   extern __shared__ float smem[];
   constexpr int ES = Elt<Tag>::bytes;
   // A block of 32 tokens is two 16-row sub-tiles (each contiguous in both
@@ -361,7 +433,16 @@ void decode_kernel(DecodeArgs a) {
 
   const int h = lane & 15;
   QFrag<Tag, D> qf;
-  qf.load(a.q + (((int64_t)seq * a.num_q_heads + head0 + (h < G ? h : 0)) * D) * ES, h < G, lane);
+  qf.load(a.q + (((int64_t)seq * a.num_q_heads + head0 + (h < G ? h : 0)) * D) * In<Tag>::bytes,
+          h < G, lane);
+  // FP8: the K scale of the head folds into the score scale, the V scale
+  // into the output.
+  float qk_scale = a.qk_scale;
+  float v_scale = 1.f;
+  if constexpr (IsFP8<Tag>::value) {
+    qk_scale *= a.k_scales[g];
+    v_scale = a.v_scales[g];
+  }
 
   State<D> st;
   st.m = -INFINITY;
@@ -383,36 +464,46 @@ void decode_kernel(DecodeArgs a) {
 
   // Blocks are processed in chunks of up to 64 per wavefront: one table load
   // per chunk, each id broadcast with readlane.
-  Frag<Tag, D> fa, fb;
-  int nva = 0, nvb = 0;
+  using CT = typename ComputeTag<Tag>::type;
+  Frag<Tag, D> f[NBuf];
+  int nv[NBuf];
   int c0 = 0, n = 0, tb = 0;
   // Block i of the chunk: physical id (0 when out of range: loads stay in
   // bounds and the block contributes nothing) and its valid-token count,
   // negated for the block that holds the current token (patched first).
   // i == n is the prefetch past the wavefront's last block: a size-0
   // resource, like a table entry outside the pool.
-  auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
+  auto load_into = [&](Frag<Tag, D>& fr, int i, int& nvr) {
     int phys = __builtin_amdgcn_readlane(tb, min(i, n - 1));
     const int j = first + kWaves * (c0 + i);
     const bool ok = i < n && phys >= 0 && phys < a.num_blocks;
-    nv = ok ? min(a.rows, L - j * a.rows) : 0;
+    nvr = ok ? min(a.rows, L - j * a.rows) : 0;
     if (!ok) phys = 0;
-    if (own_new && j == j_new) nv = -nv;
+    if (own_new && j == j_new) nvr = -nvr;
     const int64_t off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
     const int bytes = ok ? sub_bytes : 0;
-    f.load(tile_rsrc(a.k_pool + off, bytes), tile_rsrc(a.v_pool + off, bytes), lane);
+    fr.load(tile_rsrc(a.k_pool + off, bytes), tile_rsrc(a.v_pool + off, bytes), lane);
   };
-  auto attend = [&](Frag<Tag, D>& f, int nv) {
-    if (nv < 0) {
-      patch_token<Tag, D>(f, stage, o_new, lane);
-      nv = -nv;
+  auto attend_regs = [&](Frag<CT, D>& w, int nvr) {
+    if (nvr < 0) {
+      patch_token<CT, D>(w, stage, o_new, lane);
+      nvr = -nvr;
     }
-    if (nv > 0) attend_block<Tag, D>(f, qf, st, nv, a.qk_scale, lane);
+    if (nvr > 0) attend_block<CT, D>(w, qf, st, nvr, qk_scale, lane);
+  };
+  auto attend = [&](Frag<Tag, D>& fr, int nvr) {
+    if constexpr (IsFP8<Tag>::value) {
+      Frag<CT, D> w = fr.bf16();
+      attend_regs(w, nvr);
+    } else {
+      attend_regs(fr, nvr);
+    }
   };
   auto open_chunk = [&]() {
     n = min(kWave, cnt - c0);
     tb = lane < n ? trow[(first + kWaves * (c0 + lane)) / a.sub] : 0;
-    load_into(fa, 0, nva);
+#pragma unroll
+    for (int u = 0; u + 1 < NBuf; ++u) load_into(f[u], u, nv[u]);
   };
 
   if (cnt > 0) open_chunk();
@@ -420,18 +511,21 @@ void decode_kernel(DecodeArgs a) {
     tok.stage(stage);
     __syncthreads();
   }
-  // Two register buffers, one block ahead.  Loads are unconditional so that
-  // every computation waits only for its own block (a conditional load makes
-  // the wait counts path-dependent and the compiler falls back to waiting
-  // for everything); past the last block the load is an empty-resource one.
+  // A ring of NBuf register buffers, NBuf - 1 blocks ahead.  Loads are
+  // unconditional so that every computation waits only for its own block (a
+  // conditional load makes the wait counts path-dependent and the compiler
+  // falls back to waiting for everything); past the last block the load is an
+  // empty-resource one.  The ring index is a compile-time constant in the
+  // unrolled body (registers are never indexed at run time).
   for (; c0 < cnt; c0 += kWave) {
     if (c0 > 0) open_chunk();
-    for (int i = 0; i < n; i += 2) {
-      load_into(fb, i + 1, nvb);
-      attend(fa, nva);
-      if (i + 1 >= n) break;
-      load_into(fa, i + 2, nva);
-      attend(fb, nvb);
+    for (int i = 0; i < n; i += NBuf) {
+#pragma unroll
+      for (int u = 0; u < NBuf; ++u) {
+        if (i + u >= n) break;
+        load_into(f[(u + NBuf - 1) % NBuf], i + u + NBuf - 1, nv[(u + NBuf - 1) % NBuf]);
+        attend(f[u], nv[u]);
+      }
     }
   }
   // Pool write of the current token after the loop: a store while the same
@@ -472,7 +566,7 @@ void decode_kernel(DecodeArgs a) {
         den += c * sm_l[w * G + hh];
       }
     }
-    const float val = den > 0.f ? num / den : 0.f;
+    const float val = den > 0.f ? num / den * v_scale : 0.f;
     const int64_t row = (int64_t)seq * a.num_q_heads + head0 + hh;
     if (single) {
       store_out<OutT>(reinterpret_cast<OutT*>(a.out) + row * D + d, val);
@@ -605,8 +699,9 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
   const int32_t G = num_q_heads / pool->num_kv_heads;
   if (G > 16) return PA_ERR_UNSUPPORTED;
-  if (out_dtype != PA_F32 && out_dtype != pool->dtype) return PA_ERR_UNSUPPORTED;
-  const int es = elem_bytes(pool->dtype);
+  const pa_dtype out16 = pool->dtype == PA_FP8_E4M3 ? PA_BF16 : pool->dtype;
+  if (out_dtype != PA_F32 && out_dtype != out16) return PA_ERR_UNSUPPORTED;
+  const int es = input_bytes(pool->dtype);
   if (k_new) {
     if (new_stride < (int64_t)pool->num_kv_heads * pool->head_dim || (new_stride * es) % 16 ||
         !aligned16(k_new) || !aligned16(v_new))
@@ -658,6 +753,8 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   a.longest_first = 1;
 #endif
   a.qk_scale = scale * kLog2e;
+  a.k_scales = pool->k_scales;
+  a.v_scales = pool->v_scales;
   // LDS: [merge area | staged current token]; the ranking keys alias the start.
   const size_t merge = ((size_t)kWaves * G * (pool->head_dim + 2) * sizeof(float) + 15) / 16 * 16;
   a.stage_off = (int32_t)merge;
@@ -673,6 +770,9 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
     case PA_F16:
       return out_dtype == PA_F32 ? dispatch_d<TagF16, float>(D, a, units, lds, s)
                                  : dispatch_d<TagF16, _Float16>(D, a, units, lds, s);
+    case PA_FP8_E4M3:
+      return out_dtype == PA_F32 ? dispatch_d<TagFP8, float>(D, a, units, lds, s)
+                                 : dispatch_d<TagFP8, __bf16>(D, a, units, lds, s);
     case PA_F32:
       return dispatch_d<TagF32, float>(D, a, units, lds, s);
     default:

@@ -16,9 +16,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-inline int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+// Bytes per stored element, and per element of the 16-bit-or-wider inputs
+// (k_new, v_new, q): bf16 for FP8 pools.
+inline int elem_bytes(pa_dtype t) { return t == PA_F32 ? 4 : t == PA_FP8_E4M3 ? 1 : 2; }
+inline int input_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
 
-inline bool dtype_ok(pa_dtype t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
+inline bool dtype_ok(pa_dtype t) {
+  return t == PA_F32 || t == PA_F16 || t == PA_BF16 || t == PA_FP8_E4M3;
+}
 
 // Host-side validation of a pool descriptor.  Returns PA_OK or the status.
 inline pa_status check_pool(const pa_pool_desc* p) {
@@ -26,6 +31,7 @@ inline pa_status check_pool(const pa_pool_desc* p) {
   if (p->num_blocks < 1 || p->block_size < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
     return PA_ERR_INVALID_ARG;
   if (!dtype_ok(p->dtype)) return PA_ERR_UNSUPPORTED;
+  if (p->dtype == PA_FP8_E4M3 && (!p->k_scales || !p->v_scales)) return PA_ERR_INVALID_ARG;
   if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32) return PA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
   // Flat slot indices are int32.
@@ -42,5 +48,16 @@ inline pa_status launch_status() {
 }
 
 inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// E4M3 code of x / scale: the quotient in fp32 (IEEE division), clamped to
+// +-448 so that the conversion cannot overflow, rounded to nearest even by
+// the hardware conversion; NaN gives 0x7F.
+__device__ inline uint32_t fp8_code(float x, float scale) {
+  float y = x / scale;
+  if (y != y) return 0x7Fu;
+  y = y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xFFu;
+}
+__device__ inline float bf16_bits_to_float(uint32_t b16) { return __builtin_bit_cast(float, b16 << 16); }
 
 }  // namespace pa

@@ -61,6 +61,8 @@ struct PrefillArgs {
   int32_t wave_rows;         // NQ * tpg
   int32_t num_tiles;         // row tiles of kPWaves * wave_rows per sequence
   float qk_scale;            // scale * log2(e)
+  const float* k_scales;     // FP8 pools: per-KV-head scales, else null
+  const float* v_scales;
 };
 
 template <class Tag, int D, int NQ, class OutT>
@@ -105,7 +107,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     has[q] = col_ok && t < row_end && p >= 0;
     pos[q] = has[q] ? p : 0;              // idle columns see key 0 only (their q is 0)
     const int64_t qrow = has[q] ? ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) : 0;
-    qf[q].load(a.q + qrow * D * ES, has[q], lane);
+    qf[q].load(a.q + qrow * D * In<Tag>::bytes, has[q], lane);
+  }
+  // FP8: the head's K scale folds into the score scale, its V scale into the output.
+  float qk_scale = a.qk_scale;
+  float v_scale = 1.f;
+  if constexpr (Elt<Tag>::bytes == 1) {
+    qk_scale *= a.k_scales[g];
+    v_scale = a.v_scales[g];
   }
 
   // Keys 0 .. p_last, where p_last is the position of the wavefront's last row.
@@ -140,12 +149,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
                                    tile_rsrc(a.v_pool + off, bytes), lane);
   };
+  using CT = typename ComputeTag<Tag>::type;
   auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
     if (nv <= 0) return;
     const int key0 = (c0 + i) * a.rows;
+    const Frag<CT, D> w = compute_regs(f);
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
-      attend_block<Tag, D, true>(f, qf[q], st[q], nv, a.qk_scale, lane, pos[q] - key0 + 1);
+      attend_block<CT, D, true>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
   };
   auto open_chunk = [&]() {
     nc = min(kWave, cnt - c0);
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     const float l_tot = xor_sum(st[q].l);
     const int t = row0 + q * a.tpg + cr;
     if (!(col_ok && t < row_end)) continue;
-    const float inv = (has[q] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const float inv = (has[q] && l_tot > 0.f) ? v_scale / l_tot : 0.f;
     OutT* o = reinterpret_cast<OutT*>(a.out) +
               ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) * D + 4 * (lane >> 4);
 #pragma unroll
@@ -212,7 +223,8 @@ pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_pool, con
   if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
   const int32_t G = num_q_heads / pool->num_kv_heads;
   if (G > 16) return PA_ERR_UNSUPPORTED;
-  if (out_dtype != PA_F32 && out_dtype != pool->dtype) return PA_ERR_UNSUPPORTED;
+  const pa_dtype out16 = pool->dtype == PA_FP8_E4M3 ? PA_BF16 : pool->dtype;
+  if (out_dtype != PA_F32 && out_dtype != out16) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_chunk_len == 0) return PA_OK;
   if (!k_pool || !v_pool || !q || !out || !q_start || !context_lens) return PA_ERR_INVALID_ARG;
   if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
@@ -243,6 +255,8 @@ pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_pool, con
   const int32_t wg_rows = kPWaves * a.wave_rows;
   a.num_tiles = (max_chunk_len + wg_rows - 1) / wg_rows;
   a.qk_scale = scale * 1.4426950408889634f;
+  a.k_scales = pool->k_scales;
+  a.v_scales = pool->v_scales;
   const int64_t units = (int64_t)a.num_kv_heads * num_seqs * a.num_tiles;
   if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
@@ -254,6 +268,9 @@ pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_pool, con
     case PA_F16:
       return out_dtype == PA_F32 ? dispatch_prefill<TagF16, float>(D, a, units, s)
                                  : dispatch_prefill<TagF16, _Float16>(D, a, units, s);
+    case PA_FP8_E4M3:
+      return out_dtype == PA_F32 ? dispatch_prefill<TagFP8, float>(D, a, units, s)
+                                 : dispatch_prefill<TagFP8, __bf16>(D, a, units, s);
     case PA_F32:
       return dispatch_prefill<TagF32, float>(D, a, units, s);
     default:

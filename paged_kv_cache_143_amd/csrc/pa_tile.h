@@ -19,6 +19,7 @@ constexpr int kRows = 16;           // tokens per matrix-core row tile (sub-tile
 struct TagF32 {};
 struct TagF16 {};
 struct TagBF16 {};
+struct TagFP8 {};       // E4M3 storage, dequantized to bf16 in registers
 
 template <class Tag> struct Is16 { static constexpr bool value = true; };
 template <> struct Is16<TagF32> { static constexpr bool value = false; };
@@ -28,6 +29,9 @@ template <class Tag> __device__ inline f32x4 mma32(u32x4 a, u32x4 b, f32x4 c);
 template <> __device__ inline f32x4 mma32<TagBF16>(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ inline f32x4 mma32<TagFP8>(u32x4 a, u32x4 b, f32x4 c) {
+  return mma32<TagBF16>(a, b, c);
 }
 template <> __device__ inline f32x4 mma32<TagF16>(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -45,10 +49,12 @@ template <> __device__ inline uint32_t narrow16<TagBF16>(float x) {
 template <> __device__ inline uint32_t narrow16<TagF16>(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
+template <> __device__ inline uint32_t narrow16<TagFP8>(float x) { return narrow16<TagBF16>(x); }
 template <class Tag> __device__ inline float widen16(uint32_t bits);
 template <> __device__ inline float widen16<TagBF16>(uint32_t bits) {
   return __builtin_bit_cast(float, bits << 16);
 }
+template <> __device__ inline float widen16<TagFP8>(uint32_t bits) { return widen16<TagBF16>(bits); }
 template <> __device__ inline float widen16<TagF16>(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
@@ -98,6 +104,16 @@ template <int Pol = kKvCachePolicy> __device__ inline u32x4 buf_load16(rsrc_t r,
 template <int Pol = kKvCachePolicy> __device__ inline u32x2 buf_load8(rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, Pol);
 }
+template <int Pol = kKvCachePolicy> __device__ inline uint32_t buf_load4(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, Pol);
+}
+
+// Two E4M3 codes (bytes 2*hi, 2*hi+1 of w) -> two bf16 (exact: every E4M3
+// value is a bf16 value).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <bool Hi> __device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, Hi));
+}
 
 template <class Tag, int D> struct Frag<Tag, D, true> {
   static constexpr int NK = D / 32;
@@ -114,6 +130,48 @@ template <class Tag, int D> struct Frag<Tag, D, true> {
     for (int n = 0; n < NV; ++n) v[n] = buf_load8<Pol>(rv, vr + n * 128);
   }
 };
+
+// FP8 storage: the same lane roles as 16-bit with half the bytes (K: 8
+// bytes per lane and k-step, V: 4 bytes per lane and dim tile), held as raw
+// codes (16 VGPRs for 128 dims, so more sub-tiles can be in flight) and
+// converted to the bf16 registers of Frag<TagBF16> just before use.
+template <int D> struct Frag<TagFP8, D, true> {
+  u32x2 k[D / 32];
+  uint32_t v[D / 16];
+  template <int Pol = kKvCachePolicy>
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
+    const int kr = (lane & 15) * D + (lane >> 4) * 8;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) k[m] = buf_load8<Pol>(rk, kr + m * 32);
+    const int vr = (lane >> 4) * (D * 4) + (lane & 15) * 4;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) v[n] = buf_load4<Pol>(rv, vr + n * 64);
+  }
+  __device__ inline Frag<TagBF16, D, true> bf16() const {
+    Frag<TagBF16, D, true> f;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+      f.k[m] = u32x4{fp8x2_to_bf16x2<false>(k[m][0]), fp8x2_to_bf16x2<true>(k[m][0]),
+                     fp8x2_to_bf16x2<false>(k[m][1]), fp8x2_to_bf16x2<true>(k[m][1])};
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+      f.v[n] = u32x2{fp8x2_to_bf16x2<false>(v[n]), fp8x2_to_bf16x2<true>(v[n])};
+    return f;
+  }
+};
+
+// The tag the matrix-core code runs in, and the registers it reads: FP8
+// fragments convert to bf16 ones, the others are used as loaded.
+template <class Tag> struct ComputeTag { using type = Tag; };
+template <> struct ComputeTag<TagFP8> { using type = TagBF16; };
+template <class Tag> struct IsFP8 { static constexpr bool value = false; };
+template <> struct IsFP8<TagFP8> { static constexpr bool value = true; };
+template <class Tag, int D> __device__ inline Frag<Tag, D> compute_regs(const Frag<Tag, D>& f) {
+  return f;
+}
+template <int D> __device__ inline Frag<TagBF16, D> compute_regs(const Frag<TagFP8, D>& f) {
+  return f.bf16();
+}
 
 // fp32: K tile [16][d] -> load j gives lane (t = lane%16) dims
 // 4*(4j + lane/16) ..; V tile [16/4][d][4] -> load n gives lane
@@ -146,6 +204,7 @@ template <class Tag, int D> struct QFrag<Tag, D, true> {
     }
   }
 };
+template <int D> struct QFrag<TagFP8, D, true> : QFrag<TagBF16, D, true> {};
 template <class Tag, int D> struct QFrag<Tag, D, false> {
   f32x4 q[D / 16];
   __device__ inline void load(const char* qrow, bool valid, int lane) {
@@ -246,8 +305,12 @@ template <> __device__ inline void store_out<float>(float* o, float x) { *o = x;
 template <> __device__ inline void store_out<__bf16>(__bf16* o, float x) { *o = static_cast<__bf16>(x); }
 template <> __device__ inline void store_out<_Float16>(_Float16* o, float x) { *o = static_cast<_Float16>(x); }
 
+// Bytes per stored element (Elt) and per input element -- q, k_new, v_new --
+// (In): bf16 inputs for FP8 storage.
 template <class Tag> struct Elt { using T = uint16_t; static constexpr int bytes = 2; };
 template <> struct Elt<TagF32> { using T = float; static constexpr int bytes = 4; };
+template <> struct Elt<TagFP8> { using T = uint8_t; static constexpr int bytes = 1; };
+template <class Tag> struct In { static constexpr int bytes = Is16<Tag>::value ? 2 : 4; };
 
 
 }  // namespace pa

@@ -26,24 +26,32 @@ from .workloads import (APPEND, CREATE, DTYPES, FORK, RELEASE, SWAP_IN, SWAP_OUT
 class PagedKV:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
                  device: str = "cuda", poison: bool = True, block_size: int = 16,
-                 host_blocks: int = 0):
-        self.desc = B.make_desc(num_blocks, num_kv_heads, head_dim, dtype, block_size)
+                 host_blocks: int = 0, kv_scales=None):
+        # FP8 pools: per-KV-head scales live on the device beside the pools
+        self.k_scales = self.v_scales = None
+        if dtype == "fp8":
+            ks, vs = kv_scales
+            self.k_scales = torch.tensor(ks, dtype=torch.float32, device=device)
+            self.v_scales = torch.tensor(vs, dtype=torch.float32, device=device)
+        self.desc = B.make_desc(num_blocks, num_kv_heads, head_dim, dtype, block_size,
+                                self.k_scales, self.v_scales)
         self.dtype = dtype
         self.block_size = block_size
         elems = num_blocks * num_kv_heads * block_size * head_dim
         self.k = torch.empty(elems, dtype=DTYPES[dtype], device=device)
         self.v = torch.empty(elems, dtype=DTYPES[dtype], device=device)
+        nan = 0x7F if dtype == "fp8" else float("nan")     # the E4M3 NaN code
         if poison:                                   # stale/unused slots read as NaN
-            self.k.fill_(float("nan"))
-            self.v.fill_(float("nan"))
+            self.k.fill_(nan)
+            self.v.fill_(nan)
         # host swap space: pinned (page-locked) memory in the same block layout
         self.host_blocks = host_blocks
         helems = host_blocks * num_kv_heads * block_size * head_dim
         self.host_k = torch.empty(helems, dtype=DTYPES[dtype], pin_memory=host_blocks > 0)
         self.host_v = torch.empty(helems, dtype=DTYPES[dtype], pin_memory=host_blocks > 0)
         if poison:
-            self.host_k.fill_(float("nan"))
-            self.host_v.fill_(float("nan"))
+            self.host_k.fill_(nan)
+            self.host_v.fill_(nan)
 
     @property
     def num_blocks(self) -> int:
@@ -153,7 +161,7 @@ class _Flusher:
 def build_batch(w: Workload, device: str = "cuda", poison: bool = True,
                 table_width: Optional[int] = None, drop_payload_cache: bool = True) -> Batch:
     kv = PagedKV(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, device, poison, w.block_size,
-                 w.host_blocks)
+                 w.host_blocks, w.kv_scales() if w.dtype == "fp8" else None)
     bm = BlockManager(w.num_blocks, w.block_size, w.free_order, host_blocks=w.host_blocks)
     fl = _Flusher(w, kv, device)
     last: Dict[int, Tuple[int, int]] = {}
@@ -187,8 +195,8 @@ def build_batch(w: Workload, device: str = "cuda", poison: bool = True,
     lens = bm.length_array(names)
     q = w.queries().to(device)
     shape = (len(names), w.num_kv_heads, w.head_dim)
-    step_k = torch.empty(shape, dtype=DTYPES[w.dtype])
-    step_v = torch.empty(shape, dtype=DTYPES[w.dtype])
+    step_k = torch.empty(shape, dtype=DTYPES[w.input_dtype])
+    step_v = torch.empty(shape, dtype=DTYPES[w.input_dtype])
     for i, n in enumerate(names):
         key, row = last[n]
         k, v = w.kv(key)

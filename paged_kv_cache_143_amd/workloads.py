@@ -33,7 +33,11 @@ import torch
 # valid block id, so any read through it would be an out-of-range access.
 TABLE_PAD = 0x7FFFFFFF
 
-DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+# Storage dtypes.  FP8 pools store E4M3 codes (as bytes on the device); their
+# inputs (q, new K/V) are bf16.
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "fp8": torch.uint8}
+INPUT_DTYPE = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8": "bf16"}
 
 # Op kinds of an allocator script.
 CREATE, FORK, APPEND, RELEASE = "create", "fork", "append", "release"
@@ -100,11 +104,29 @@ class Workload:
     # newest tokens (payload rows L-n .. L-1 of key i); None for decode.
     chunk_lens: Optional[List[int]] = None
     host_blocks: int = 0            # host swap space, in blocks
+    # FP8 pools: per-KV-head scales (fp32 values); drawn from the seed when None
+    k_scales: Optional[List[float]] = None
+    v_scales: Optional[List[float]] = None
     _cache: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = field(default_factory=dict, repr=False)
 
     @property
     def num_seqs(self) -> int:
         return len(self.seq_names)
+
+    @property
+    def input_dtype(self) -> str:
+        return INPUT_DTYPE[self.dtype]
+
+    def kv_scales(self) -> Tuple[List[float], List[float]]:
+        """FP8 pools: (K, V) scale per KV head.  Default: (3 + 2u) / 448 with u
+        uniform per head, i.e. about 3..5 standard deviations map to the
+        largest code, so a few of the N(0,1) values saturate."""
+        if self.k_scales is not None and self.v_scales is not None:
+            return list(self.k_scales), list(self.v_scales)
+        rng = np.random.default_rng(_mix(self.seed, 5))
+        u = rng.random((2, self.num_kv_heads))
+        sc = ((3.0 + 2.0 * u) / 448.0).astype(np.float32)
+        return [float(x) for x in sc[0]], [float(x) for x in sc[1]]
 
     @property
     def scale(self) -> float:
@@ -116,8 +138,8 @@ class Workload:
         if key not in self._cache:
             n = self.data_len[key]
             shape = (n, self.num_kv_heads, self.head_dim)
-            k = normal(shape, (self.seed, 1, key), self.dtype)
-            v = normal(shape, (self.seed, 2, key), self.dtype)
+            k = normal(shape, (self.seed, 1, key), self.input_dtype)
+            v = normal(shape, (self.seed, 2, key), self.input_dtype)
             self._cache[key] = (k, v)
         return self._cache[key]
 
@@ -126,17 +148,18 @@ class Workload:
 
     def queries(self) -> torch.Tensor:
         """q [num_seqs, Hq, d] in the dtype, one draw per sequence name."""
-        rows = [normal((self.num_q_heads, self.head_dim), (self.seed, 3, n), self.dtype)
+        rows = [normal((self.num_q_heads, self.head_dim), (self.seed, 3, n), self.input_dtype)
                 for n in self.seq_names]
         return torch.stack(rows) if rows else torch.empty(
-            (0, self.num_q_heads, self.head_dim), dtype=DTYPES[self.dtype])
+            (0, self.num_q_heads, self.head_dim), dtype=DTYPES[self.input_dtype])
 
     def chunk_queries(self) -> torch.Tensor:
         """q rows [sum(chunk_lens), Hq, d] of the chunks, sequence by sequence."""
-        rows = [normal((int(n), self.num_q_heads, self.head_dim), (self.seed, 4, name), self.dtype)
+        rows = [normal((int(n), self.num_q_heads, self.head_dim), (self.seed, 4, name),
+                       self.input_dtype)
                 for name, n in zip(self.seq_names, self.chunk_lens)]
         return torch.cat(rows) if rows else torch.empty(
-            (0, self.num_q_heads, self.head_dim), dtype=DTYPES[self.dtype])
+            (0, self.num_q_heads, self.head_dim), dtype=DTYPES[self.input_dtype])
 
 
 def _uniform_lengths(rng: np.random.Generator, n: int, lo: int, hi: int) -> List[int]:
@@ -375,6 +398,14 @@ def swap_gqa_bf16(num_seqs: int = 256, seed: int = 8) -> Workload:
     rng = np.random.default_rng(seed + 100)
     lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
     return swap_cycle("swap-gqa-bf16", seed, "bf16", lengths, 32, 8, 128)
+
+
+def gqa_fp8(num_seqs: int = 256, seed: int = 3) -> Workload:
+    """The batch-256 GQA workload (same lengths and values) on an FP8 E4M3 cache."""
+    rng = np.random.default_rng(seed + 100)
+    lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
+    return independent("gqa-fp8-b256", seed, "fp8", lengths, 32, 8, 128,
+                       _pool_for(lengths, 16, 0.0))
 
 
 def gqa_bf16_in_order(num_seqs: int = 256, seed: int = 3) -> Workload:

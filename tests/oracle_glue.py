@@ -11,6 +11,7 @@ import torch
 from oracle.allocator import BlockModel, run_script
 from oracle.pool import SlotPool
 from oracle import attention as OA
+from oracle import fp8 as OF8
 from oracle import prefill as OPF
 
 
@@ -24,12 +25,35 @@ class OracleRun:
         self._f64: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
 
     def resolve(self, payload):
+        """fp64 K, V rows of a payload as the pool holds them: the generated
+        values, or for FP8 pools value(code) * scale of each KV head."""
         key, row = payload
         if key not in self._f64:
             k, v = self.w.kv(key)
-            self._f64[key] = (k.to(torch.float64).numpy(), v.to(torch.float64).numpy())
+            k, v = k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
+            if self.w.dtype == "fp8":
+                ks, vs = self.w.kv_scales()
+                k, v = k.copy(), v.copy()
+                for g in range(self.w.num_kv_heads):
+                    k[:, g] = OF8.dequantize(OF8.quantize(k[:, g], ks[g]), ks[g])
+                    v[:, g] = OF8.dequantize(OF8.quantize(v[:, g], vs[g]), vs[g])
+            self._f64[key] = (k, v)
         k, v = self._f64[key]
         return k[row], v[row]
+
+    def resolve_codes(self, payload):
+        """FP8 pools: the E4M3 codes of a payload's K, V rows, as floats with
+        the NaN codes as NaN (for bit-exact pool comparison)."""
+        key, row = payload
+        k, v = self.w.kv(key)
+        ks, vs = self.w.kv_scales()
+        kc = np.stack([OF8.quantize(k[row, g].float().numpy(), ks[g])
+                       for g in range(self.w.num_kv_heads)]).astype(np.float64)
+        vc = np.stack([OF8.quantize(v[row, g].float().numpy(), vs[g])
+                       for g in range(self.w.num_kv_heads)]).astype(np.float64)
+        kc[(kc == 0x7F) | (kc == 0xFF)] = np.nan
+        vc[(vc == 0x7F) | (vc == 0xFF)] = np.nan
+        return kc, vc
 
     @property
     def tables(self):
