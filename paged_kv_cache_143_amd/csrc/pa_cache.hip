@@ -79,8 +79,8 @@ __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_
 }
 
 // FP8 pools: bf16 inputs; a thread quantizes 16 consecutive dims of one
-// (token, head) with that head's scales into one 16-byte K store (the
-// token's row) and 16 one-byte V stores 4 bytes apart (4 tokens interleaved).
+// (token, head) with that head's scales into one 16-byte K store and 16
+// one-byte V stores, at the offsets of the FP8 tile layout.
 __device__ inline uint32_t pack4_fp8(const u32x4& a, const u32x4& b, int q, float scale) {
   uint32_t w = 0;
 #pragma unroll
@@ -121,16 +121,18 @@ __global__ void write_kv_fp8_kernel(char* __restrict__ k_pool, char* __restrict_
   u32x4 kc;
 #pragma unroll
   for (int q = 0; q < 4; ++q) kc[q] = pack4_fp8(k0, k1, q, ks);
-  *reinterpret_cast<u32x4*>(k_pool + tile + (int64_t)off * head_dim + (int64_t)c * X) = kc;
+  // 16 consecutive dims starting at a multiple of 16 are one 16-byte piece
+  *reinterpret_cast<u32x4*>(k_pool + tile + fp8_k_offset(off, c * X, block_size, head_dim)) = kc;
   const u32x4 v0 = *reinterpret_cast<const u32x4*>(v_new + src);
   const u32x4 v1 = *reinterpret_cast<const u32x4*>(v_new + src + 16);
   const float vs = v_scales[h];
-  char* vb = v_pool + tile + ((int64_t)(off >> 2) * head_dim + (int64_t)c * X) * 4 + (off & 3);
+  char* vt = v_pool + tile;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t w = pack4_fp8(v0, v1, q, vs);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vb[(int64_t)(4 * q + j) * 4] = (char)((w >> (8 * j)) & 0xFFu);
+    for (int j = 0; j < 4; ++j)
+      vt[fp8_v_offset(off, c * X + 4 * q + j, block_size, head_dim)] = (char)((w >> (8 * j)) & 0xFFu);
   }
 }
 

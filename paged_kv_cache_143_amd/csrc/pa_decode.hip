@@ -200,12 +200,15 @@ __device__ inline int seq_of_rank_pairwise(const DecodeArgs& a, int r, int* lds)
 // The fused step writes the current token (offset o of its block) to the pool
 // and, for the one block that holds it, replaces the loaded values of that
 // token with the staged copy -- the tile load may have raced the store.
-template <class Tag, int D>
+// Perm: the dimension order of FP8 storage (see Frag<TagFP8>).
+template <class Tag, int D, bool Perm = false>
 __device__ inline void patch_token(Frag<Tag, D, true>& f, const char* stage, int o, int lane) {
   if ((lane & 15) == o) {
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m)
-      f.k[m] = *reinterpret_cast<const u32x4*>(stage + (4 * m + (lane >> 4)) * 16);
+    for (int m = 0; m < D / 32; ++m) {
+      const int dim0 = Perm ? (lane >> 4) * (D / 4) + 8 * m : 8 * (4 * m + (lane >> 4));
+      f.k[m] = *reinterpret_cast<const u32x4*>(stage + dim0 * 2);
+    }
   }
   // Element indices below are runtime values: select, never index registers
   // dynamically (that would move the fragment to scratch memory).
@@ -216,14 +219,15 @@ __device__ inline void patch_token(Frag<Tag, D, true>& f, const char* stage, int
     const bool second = (o & 2) != 0;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
-      const uint32_t val = *reinterpret_cast<const uint16_t*>(stage + D * 2 + (16 * n + dl) * 2);
+      const int dim = Perm ? dl * (D / 16) + n : 16 * n + dl;
+      const uint32_t val = *reinterpret_cast<const uint16_t*>(stage + D * 2 + dim * 2);
       const uint32_t w0 = f.v[n][0], w1 = f.v[n][1];
       f.v[n][0] = second ? w0 : (w0 & keep) | (val << shift);
       f.v[n][1] = second ? (w1 & keep) | (val << shift) : w1;
     }
   }
 }
-template <class Tag, int D>
+template <class Tag, int D, bool Perm = false>
 __device__ inline void patch_token(Frag<Tag, D, false>& f, const char* stage, int o, int lane) {
   if ((lane & 15) == o) {
 #pragma unroll
@@ -303,8 +307,8 @@ template <class Tag, int D> struct NewToken {
 
 // FP8 pools: the bf16 current token is quantized with its head's scales when
 // loaded; the stage holds the dequantized codes (what a read of the pool
-// returns, unscaled), and the store writes the codes -- K as one 8-byte row
-// piece per thread, V as bytes 4 apart.
+// returns, unscaled), and the store writes the codes at the FP8 tile
+// layout's offsets -- K as one 8-byte piece per thread, V as bytes.
 template <int D> struct NewToken<TagFP8, D> {
   static constexpr int NC = D / 8;            // 16-byte bf16 input vectors per head row
   uint32_t code[2];                           // the thread's 8 E4M3 codes
@@ -353,12 +357,14 @@ template <int D> struct NewToken<TagFP8, D> {
     const int c = is_v ? t - NC : t;
     char* tile = (is_v ? a.v_pool : a.k_pool) + ((int64_t)phys * a.num_kv_heads + g) * kTile;
     if (!is_v) {
-      *reinterpret_cast<u32x2*>(tile + (int64_t)o * D + c * 8) = u32x2{code[0], code[1]};
+      // 8 consecutive dims from a multiple of 8: contiguous in a 16-byte piece
+      *reinterpret_cast<u32x2*>(tile + fp8_k_offset(o, c * 8, a.block_size, D)) =
+          u32x2{code[0], code[1]};
     } else {
-      char* vb = tile + (int64_t)(o >> 2) * D * 4 + (o & 3);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vb[(int64_t)(c * 8 + e) * 4] = (char)((code[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        tile[fp8_v_offset(o, c * 8 + e, a.block_size, D)] =
+            (char)((code[e >> 2] >> (8 * (e & 3))) & 0xFFu);
     }
   }
 };
@@ -482,11 +488,11 @@ void decode_kernel(DecodeArgs a) {
     if (own_new && j == j_new) nvr = -nvr;
     const int64_t off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
     const int bytes = ok ? sub_bytes : 0;
-    fr.load(tile_rsrc(a.k_pool + off, bytes), tile_rsrc(a.v_pool + off, bytes), lane);
+    fr.load(tile_rsrc(a.k_pool + off, bytes), tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
   };
   auto attend_regs = [&](Frag<CT, D>& w, int nvr) {
     if (nvr < 0) {
-      patch_token<CT, D>(w, stage, o_new, lane);
+      patch_token<CT, D, IsFP8<Tag>::value>(w, stage, o_new, lane);
       nvr = -nvr;
     }
     if (nvr > 0) attend_block<CT, D>(w, qf, st, nvr, qk_scale, lane);
@@ -542,11 +548,11 @@ void decode_kernel(DecodeArgs a) {
       sm_m[wave * G + h] = st.m;
       sm_l[wave * G + h] = l_tot;
     }
-    float* dst = sm_a + ((int64_t)wave * G + h) * D + 4 * (lane >> 4);
+    float* dst = sm_a + ((int64_t)wave * G + h) * D;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[16 * n + r] = st.acc[n][r];
+      for (int r = 0; r < 4; ++r) dst[out_dim<Tag, D>(n, r, lane)] = st.acc[n][r];
   }
   __syncthreads();
 

@@ -60,4 +60,21 @@ __device__ inline uint32_t fp8_code(float x, float scale) {
 }
 __device__ inline float bf16_bits_to_float(uint32_t b16) { return __builtin_bit_cast(float, b16 << 16); }
 
+// Byte offsets of (token t, dim d) inside one FP8 (block, KV head) tile of b
+// tokens and D dims: sub-tiles of R = min(b, 16) tokens, each
+//   K: [g < 4][h < D/64][row < R][16 bytes], dim d = g*D/4 + 16h + byte;
+//   V: [tg < R/4][h < D/64][r < 16][4 dims][4 tokens], dim d = r*D/16 + 4h + e.
+__device__ inline int fp8_k_offset(int t, int d, int b, int D) {
+  const int R = b < 16 ? b : 16;
+  const int s = t / R, tl = t - s * R;
+  const int g = d / (D / 4), w = d - g * (D / 4);
+  return s * R * D + g * (R * D / 4) + (w >> 4) * (R * 16) + tl * 16 + (w & 15);
+}
+__device__ inline int fp8_v_offset(int t, int d, int b, int D) {
+  const int R = b < 16 ? b : 16;
+  const int s = t / R, tl = t - s * R;
+  const int r = d / (D / 16), w = d - r * (D / 16);
+  return s * R * D + (tl >> 2) * (4 * D) + (w >> 2) * 256 + r * 16 + (w & 3) * 4 + (tl & 3);
+}
+
 }  // namespace pa

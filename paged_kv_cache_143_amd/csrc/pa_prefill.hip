@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     const int64_t off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
     const int bytes = ok ? sub_bytes : 0;
     f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
-                                   tile_rsrc(a.v_pool + off, bytes), lane);
+                                   tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
   };
   using CT = typename ComputeTag<Tag>::type;
   auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     const Frag<CT, D> w = compute_regs(f);
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
-      attend_block<CT, D, true>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
+      attend_block<CT, D>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
   };
   auto open_chunk = [&]() {
     nc = min(kWave, cnt - c0);
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // Normalise and store: lane holds dims 16k + 4(lane/16) .. +3 of its column.
+  // Normalise and store: acc[k][r] is output dim out_dim(k, r) of the lane's column.
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const float l_tot = xor_sum(st[q].l);
@@ -183,11 +183,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     if (!(col_ok && t < row_end)) continue;
     const float inv = (has[q] && l_tot > 0.f) ? v_scale / l_tot : 0.f;
     OutT* o = reinterpret_cast<OutT*>(a.out) +
-              ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) * D + 4 * (lane >> 4);
+              ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) * D;
 #pragma unroll
     for (int k = 0; k < D / 16; ++k)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) store_out<OutT>(o + 16 * k + r, st[q].acc[k][r] * inv);
+      for (int r = 0; r < 4; ++r) store_out<OutT>(o + out_dim<Tag, D>(k, r, lane), st[q].acc[k][r] * inv);
   }
 }
 

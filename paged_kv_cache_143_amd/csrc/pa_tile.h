@@ -121,7 +121,7 @@ template <class Tag, int D> struct Frag<Tag, D, true> {
   u32x4 k[NK];
   u32x2 v[NV];
   template <int Pol = kKvCachePolicy>
-  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane, int = kRows) {
     const int kr = (lane & 15) * (D * 2) + (lane >> 4) * 16;
 #pragma unroll
     for (int m = 0; m < NK; ++m) k[m] = buf_load16<Pol>(rk, kr + m * 64);
@@ -131,21 +131,37 @@ template <class Tag, int D> struct Frag<Tag, D, true> {
   }
 };
 
-// FP8 storage: the same lane roles as 16-bit with half the bytes (K: 8
-// bytes per lane and k-step, V: 4 bytes per lane and dim tile), held as raw
-// codes (16 VGPRs for 128 dims, so more sub-tiles can be in flight) and
-// converted to the bf16 registers of Frag<TagBF16> just before use.
+// FP8 storage.  The memory system here is bound by requests (cache-line
+// pieces per instruction), not bytes, so the FP8 tile layout makes every
+// load instruction cover whole 128-byte lines, and the lane roles permute
+// dimensions to match (a dot product and an output row do not care about
+// the order of dimensions).  Per sub-tile of R rows (R = min(b, 16)):
+//   K: [g < 4][h < D/64][t < R][16 bytes]: lane (t, g) holds dims
+//      g*D/4 .. g*D/4 + D/4 - 1 of row t, 16 per load; k-step m of the
+//      score product uses dims g*D/4 + 8m .. +7 (the q fragment matches);
+//   V: [tg < R/4][h < D/64][r < 16][4 dims][4 tokens]: lane (r, tg) holds
+//      dims r*D/16 .. +D/16 - 1 of tokens 4tg .. 4tg+3; dim tile n of the
+//      P.V product is dim r*D/16 + n of row r (outputs permuted alike).
+// Rows past R read past the sub-tile's resource (zeros) or alias other rows;
+// either way they are masked.  Codes are converted to the bf16 registers of
+// Frag<TagBF16> just before use.
 template <int D> struct Frag<TagFP8, D, true> {
   u32x2 k[D / 32];
   uint32_t v[D / 16];
   template <int Pol = kKvCachePolicy>
-  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
-    const int kr = (lane & 15) * D + (lane >> 4) * 8;
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane, int rows = kRows) {
+    const int t = lane & 15, g = lane >> 4;
+    const int kb = g * (rows * D / 4) + t * 16;
+    const int vb = g * (4 * D) + t * 16;
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) k[m] = buf_load8<Pol>(rk, kr + m * 32);
-    const int vr = (lane >> 4) * (D * 4) + (lane & 15) * 4;
+    for (int h = 0; h < D / 64; ++h) {
+      const u32x4 a = buf_load16<Pol>(rk, kb + h * rows * 16);
+      k[2 * h] = u32x2{a[0], a[1]};
+      k[2 * h + 1] = u32x2{a[2], a[3]};
+      const u32x4 b = buf_load16<Pol>(rv, vb + h * 256);
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) v[n] = buf_load4<Pol>(rv, vr + n * 64);
+      for (int e = 0; e < 4; ++e) v[4 * h + e] = b[e];
+    }
   }
   __device__ inline Frag<TagBF16, D, true> bf16() const {
     Frag<TagBF16, D, true> f;
@@ -182,7 +198,7 @@ template <class Tag, int D> struct Frag<Tag, D, false> {
   f32x4 k[NK];
   f32x4 v[NV];
   template <int Pol = kKvCachePolicy>
-  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane) {
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane, int = kRows) {
     const int kr = (lane & 15) * (D * 4) + (lane >> 4) * 16;
 #pragma unroll
     for (int j = 0; j < NK; ++j) k[j] = __builtin_bit_cast(f32x4, buf_load16<Pol>(rk, kr + j * 64));
@@ -204,7 +220,16 @@ template <class Tag, int D> struct QFrag<Tag, D, true> {
     }
   }
 };
-template <int D> struct QFrag<TagFP8, D, true> : QFrag<TagBF16, D, true> {};
+// FP8: k-step m of lane group g uses dims g*D/4 + 8m .. +7 (the K layout above).
+template <int D> struct QFrag<TagFP8, D, true> : QFrag<TagBF16, D, true> {
+  __device__ inline void load(const char* qrow, bool valid, int lane) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const int dim0 = (lane >> 4) * (D / 4) + 8 * m;
+      this->q[m] = valid ? *reinterpret_cast<const u32x4*>(qrow + dim0 * 2) : u32x4{0, 0, 0, 0};
+    }
+  }
+};
 template <class Tag, int D> struct QFrag<Tag, D, false> {
   f32x4 q[D / 16];
   __device__ inline void load(const char* qrow, bool valid, int lane) {
@@ -219,17 +244,24 @@ template <class Tag, int D> struct QFrag<Tag, D, false> {
 // Running softmax state of one wavefront: lane (h + 16 q) owns head h;
 // acc[n][r] is output dim 16n + 4q + r of that head (the MFMA C layout).
 template <int D> struct State {
-  float m;      // running max (log2 domain), identical across the head's lanes
+  float m;      // exponent base of l and acc (log2 domain), identical across
+                // the head's lanes: the running max, moved only when a score
+                // exceeds it by more than kRescaleLog2
   float l;      // this lane's share of the running sum
   f32x4 acc[D / 16];
 };
 
+// Scores may exceed the exponent base by up to this much (p <= 2^8) before
+// the base moves; exp2(s - m) then never overflows and the softmax is the
+// same for any base.
+constexpr float kRescaleLog2 = 8.f;
+
 // One sub-tile: S = K q^T, online-softmax update of (m, l), acc += V^T P.
 // n_valid: stored tokens in the sub-tile (rows past it may hold anything).
-// Causal: a column may see none of the sub-tile's rows while its state is
-// still empty (m = -inf); the exponent base then falls back to 0 so that
-// -inf - -inf never occurs.
-template <class Tag, int D, bool Causal = false>
+// A column may see none of the sub-tile's rows while its state is still
+// empty (m = -inf, e.g. under a causal limit); its exponent base then falls
+// back to 0 so that -inf - -inf never occurs.
+template <class Tag, int D>
 __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& qf, State<D>& st,
                                     int n_valid, float qk_scale, int lane, int lim = kRows) {
   // 1) scores S[t][h]: lane (h + 16q) gets tokens 4q..4q+3 of head h.
@@ -251,18 +283,30 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
     // column's last visible row + 1) is the causal limit of multi-token queries.
     if (t0 + r >= n_valid || t0 + r >= lim) s[r] = -INFINITY;
   }
-  // 2) online softmax.
-  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  bm = xor_max(bm);
-  const float m_new = fmaxf(st.m, bm);
-  const float m_base = (Causal && m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_base);
+  // 2) online softmax with a lazily moved base: only when some score of the
+  // wavefront exceeds its column's base by more than kRescaleLog2 (always on
+  // the first sub-tile, where m = -inf) does the wavefront take the column
+  // maxima across lanes and rescale l and acc -- a uniform branch; otherwise
+  // both are skipped.
+  bool over = false;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) over |= s[r] > st.m + kRescaleLog2;
+  if (__builtin_amdgcn_ballot_w64(over) != 0) {
+    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    bm = xor_max(bm);
+    const float m_new = fmaxf(st.m, bm);
+    const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.f : m_new));
+    st.l *= alpha;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) st.acc[n] *= alpha;
+    st.m = m_new;
+  }
+  const float base = st.m == -INFINITY ? 0.f : st.m;
   float p[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - m_base);
-  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  st.m = m_new;
-  // 3) acc[d][h] = alpha * acc + V^T P.
+  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - base);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  // 3) acc[d][h] += V^T P.
   if constexpr (Is16<Tag>::value) {
     uint32_t hi[4], lo[4];
 #pragma unroll
@@ -282,7 +326,6 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
     for (int n = 0; n < D / 16; ++n) {
       const uint32_t a0 = f.v[n][0] & keep0, a1 = f.v[n][1] & keep1;
       const u32x4 va = {a0, a1, a0, a1};
-      st.acc[n] *= alpha;
       st.acc[n] = mma32<Tag>(va, pb, st.acc[n]);
     }
   } else {
@@ -293,11 +336,18 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
 #pragma unroll
         for (int e = 0; e < 4; ++e) va[e] = (t0 + e < n_valid) ? va[e] : 0.f;
       }
-      st.acc[n] *= alpha;
 #pragma unroll
       for (int e = 0; e < 4; ++e) st.acc[n] = mma4(va[e], p[e], st.acc[n]);
     }
   }
+}
+
+// Output dimension of accumulator element acc[n][i] (the MFMA C layout puts
+// row 4*(lane/16) + i of dim tile n in this lane): 16n + row, or for FP8
+// storage row*D/16 + n (the V layout's permutation).
+template <class Tag, int D> __device__ inline int out_dim(int n, int i, int lane) {
+  const int row = 4 * (lane >> 4) + i;
+  return IsFP8<Tag>::value ? row * (D / 16) + n : 16 * n + row;
 }
 
 template <class OutT> __device__ inline void store_out(OutT* o, float x);

@@ -33,19 +33,41 @@ def require_gpu():
     assert B.single_hip_runtime(), "two HIP runtimes are loaded"
 
 
+def _fp8_tile_index(b: int, D: int):
+    """Byte index of (token, dim) in one FP8 tile, from include/pa.h's layout:
+    sub-tiles of R = min(b, 16) tokens; K [g][h][row][16], V [tg][h][r][4 dims][4 tok]."""
+    R = min(b, 16)
+    t = np.arange(b)[:, None]
+    d = np.arange(D)[None, :]
+    s, tl = t // R, t % R
+    g, w = d // (D // 4), d % (D // 4)
+    k = s * R * D + g * (R * D // 4) + (w // 16) * (R * 16) + tl * 16 + (w % 16)
+    r, w2 = d // (D // 16), d % (D // 16)
+    v = s * R * D + (tl // 4) * (4 * D) + (w2 // 4) * 256 + r * 16 + (w2 % 4) * 4 + (tl % 4)
+    return k, v
+
+
 def pool_logical(kv, num_kv_heads: int, head_dim: int):
     """Device pools -> fp64 CPU arrays [blocks][offset][head][dim], read through the
-    pool layout of include/pa.h (K tiles [b][d]; V tiles [b/4][d][4])."""
+    pool layout of include/pa.h (K tiles [b][d]; V tiles [b/4][d][4]; FP8 tiles
+    in their own permuted layout, returned as codes with the NaN codes as NaN)."""
+    if kv.dtype == "fp8":
+        b = kv.block_size
+        nb = kv.k.numel() // (num_kv_heads * b * head_dim)
+        ki, vi = _fp8_tile_index(b, head_dim)
+        kt = kv.k.view(nb, num_kv_heads, b * head_dim).cpu().numpy()
+        vt = kv.v.view(nb, num_kv_heads, b * head_dim).cpu().numpy()
+        k = kt[:, :, ki].transpose(0, 2, 1, 3).astype(np.float64)     # [nb][b][H][D]
+        v = vt[:, :, vi].transpose(0, 2, 1, 3).astype(np.float64)
+        for a in (k, v):
+            a[(a == 0x7F) | (a == 0xFF)] = np.nan
+        return k, v
     b = kv.block_size
     nb = kv.k.numel() // (num_kv_heads * b * head_dim)
     k = kv.k.view(nb, num_kv_heads, b, head_dim).permute(0, 2, 1, 3)
     v = kv.v.view(nb, num_kv_heads, b // 4, head_dim, 4).permute(0, 2, 4, 1, 3)
     v = v.reshape(nb, b, num_kv_heads, head_dim)
-    k, v = k.to(torch.float64).cpu().numpy(), v.to(torch.float64).cpu().numpy()
-    if kv.dtype == "fp8":                      # codes; the two NaN codes as NaN
-        for a in (k, v):
-            a[(a == 0x7F) | (a == 0xFF)] = np.nan
-    return k, v
+    return (k.to(torch.float64).cpu().numpy(), v.to(torch.float64).cpu().numpy())
 
 
 def assert_pool_equal(got: np.ndarray, want: np.ndarray) -> None:
