@@ -53,19 +53,28 @@
  *   (blk * Hkv + h) * block_size * head_dim, so every (block, KV head) tile is
  *   one contiguous run: 4 KiB for 16 x 128 16-bit or 16 x 64 fp32 elements,
  *   2 KiB at block_size 8, 8 KiB at block_size 32.
- *   Inside a tile:
- *     K: element (offset o, dim d) at o * head_dim + d
- *        -- token-major: one token's K is one contiguous row;
- *     V: element (offset o, dim d) at ((o / 4) * head_dim + d) * 4 + o % 4
+ *   Inside a tile, with R = min(block_size, 16) and tokens split into
+ *   sub-tiles of R consecutive offsets (sub-tile s = o / R, row r = o % R,
+ *   each sub-tile R * head_dim contiguous elements, in order):
+ *     K, 16-bit pools: element (o, d) of sub-tile s at
+ *          s*R*head_dim + (d / 32) * R*32 + r*32 + d % 32   ("[d/32][R][32]");
+ *     K, fp32 pools: element (o, d) at o * head_dim + d (token-major);
+ *     V: element (o, d) at ((o / 4) * head_dim + d) * 4 + o % 4
  *        -- groups of 4 tokens interleaved per dim ("[b/4][d][4]").
- *   The decode kernel reads both with full 128-byte lines per instruction,
- *   each lane receiving its matrix-core operand directly (a token's 8 dims of
- *   K; 4 consecutive tokens of one dim of V), and a token write touches
- *   2 lines of K and 8 lines of V for 128 16-bit dims.
+ *   The decode kernel's matrix-core loads then read whole 128-byte lines
+ *   (1 KiB contiguous per 16-bit K instruction), each lane receiving its
+ *   operand directly (8 dims of one token of K; 4 consecutive tokens of one
+ *   dim of V); a token write touches 4 lines of K and 8 lines of V for 128
+ *   16-bit dims.
  *
  * FP8 pools (PA_FP8_E4M3: OCP E4M3 without infinities, max 448, all-ones
- * mantissa and exponent = NaN; one byte per element, same layout) store codes
- * with per-KV-head scales from the descriptor.  The FP8 cache exists and its
+ * mantissa and exponent = NaN; one byte per element) store codes with
+ * per-KV-head scales from the descriptor, in sub-tiles of R rows (as above)
+ * laid out for whole-line loads with permuted dimensions (D = head_dim):
+ *     K: byte (r, d) at s*R*D + (d / (D/4)) * R*D/4 + ((d % (D/4)) / 16) * R*16
+ *          + r*16 + d % 16;
+ *     V: byte (r, d) at s*R*D + (r / 4) * 4*D + ((d % (D/16)) / 4) * 256
+ *          + (d / (D/16)) * 16 + (d % 4) * 4 + r % 4.  The FP8 cache exists and its
  * usability depends on device, backend and scales ("Inside vLLM and TGI",
  * section "Launch a pinned engine from already reviewed local artifacts");
  * format and scaling here are this library's choice.  Writing value x of

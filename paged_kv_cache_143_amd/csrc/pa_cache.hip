@@ -37,8 +37,9 @@ __global__ void slot_mapping_kernel(const int32_t* __restrict__ tables, int32_t 
 
 // ---------------------------------------------------------------------------
 // Token writes.  One thread moves one 16-byte vector of X consecutive dims of
-// one (token, KV head).  K tiles are token-major ([b][d]): the vector is one
-// 16-byte store and a token's row is contiguous.  V tiles interleave groups of
+// one (token, KV head).  16-bit K tiles are sub-tiled ([d/32][R][4][8] per R
+// = min(b, 16) rows): the vector is one 16-byte store, a token's row four
+// 64-byte pieces; fp32 K tiles are token-major.  V tiles interleave groups of
 // 4 tokens per dim ([b/4][d][4]): X element stores, stride 4 elements.
 // ---------------------------------------------------------------------------
 template <int ES>  // element size in bytes: 2 or 4
@@ -63,7 +64,10 @@ __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_
   const int64_t src = ((int64_t)t * new_stride + (int64_t)h * head_dim + (int64_t)c * X) * ES;
   const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)block_size * head_dim;  // elements
   const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + src);
-  *reinterpret_cast<u32x4*>(k_pool + (tile + (int64_t)off * head_dim + (int64_t)c * X) * ES) = kv;
+  if constexpr (ES == 2)      // 16-bit K: sub-tiled layout, one 16-byte piece
+    *reinterpret_cast<u32x4*>(k_pool + tile * ES + k16_offset(off, c * X, block_size, head_dim)) = kv;
+  else                        // fp32 K: token-major rows
+    *reinterpret_cast<u32x4*>(k_pool + (tile + (int64_t)off * head_dim + (int64_t)c * X) * ES) = kv;
   const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + src);
   char* vb = v_pool + (tile + ((int64_t)(off >> 2) * head_dim + (int64_t)c * X) * 4 + (off & 3)) * ES;
   if constexpr (ES == 4) {

@@ -248,9 +248,9 @@ __device__ inline void patch_token(Frag<Tag, D, false>& f, const char* stage, in
 // The current token's K/V for KV head g: loaded into registers when the
 // workgroup starts (one 16-byte vector per thread), staged in LDS once the
 // first blocks are in flight (for patch_token), and stored to its slot after
-// the block loop -- K as 16-byte vectors of the token's contiguous row (two
-// 128-byte lines for 128 bf16 dims), V as elements interleaved by 4 tokens
-// (eight lines).  Writes cost per line touched while reads stream.
+// the block loop -- K as 16-byte vectors (four 64-byte pieces in four lines
+// for 128 bf16 dims), V as elements interleaved by 4 tokens (eight lines).
+// Writes cost per line touched while reads stream.
 template <class Tag, int D> struct NewToken {
   static constexpr int ES = Is16<Tag>::value ? 2 : 4;
   static constexpr int X = 16 / ES;
@@ -288,7 +288,10 @@ template <class Tag, int D> struct NewToken {
     const int c = is_v ? t - NC : t;
     char* tile = (is_v ? a.v_pool : a.k_pool) + ((int64_t)phys * a.num_kv_heads + g) * kTile;
     if (!is_v) {
-      *reinterpret_cast<u32x4*>(tile + ((int64_t)o * D + c * X) * ES) = vec;
+      if constexpr (ES == 2)
+        *reinterpret_cast<u32x4*>(tile + k16_offset(o, c * X, a.block_size, D)) = vec;
+      else
+        *reinterpret_cast<u32x4*>(tile + ((int64_t)o * D + c * X) * ES) = vec;
     } else {
       char* vb = tile + ((int64_t)(o >> 2) * D * 4 + (o & 3)) * ES;
 #pragma unroll

@@ -60,6 +60,16 @@ __device__ inline uint32_t fp8_code(float x, float scale) {
 }
 __device__ inline float bf16_bits_to_float(uint32_t b16) { return __builtin_bit_cast(float, b16 << 16); }
 
+// Byte offset of K elements d .. d+7 (d a multiple of 8) of token t inside one
+// 16-bit (block, KV head) tile of b tokens and D dims: sub-tiles of
+// R = min(b, 16) tokens, each [D/32][R][4][8 elements] -- a matrix-core load
+// of 16 rows then reads 1 KiB contiguous.
+__device__ inline int k16_offset(int t, int d, int b, int D) {
+  const int R = b < 16 ? b : 16;
+  const int s = t / R, tl = t - s * R;
+  return (s * R * D + (d >> 5) * (R * 32) + tl * 32 + (d & 31)) * 2;
+}
+
 // Byte offsets of (token t, dim d) inside one FP8 (block, KV head) tile of b
 // tokens and D dims: sub-tiles of R = min(b, 16) tokens, each
 //   K: [g < 4][h < D/64][row < R][16 bytes], dim d = g*D/4 + 16h + byte;

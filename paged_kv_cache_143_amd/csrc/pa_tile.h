@@ -73,10 +73,11 @@ __device__ inline float xor_sum(float v) {
 }
 
 // ---- per-block register fragments ------------------------------------------
-// 16-bit: K tile [16][d] -> load m gives lane (t = lane%16) the 8 dims
-// 8*(4m + lane/16) .. of its token (16 bytes); V tile [16/4][d][4] -> load n
-// gives lane (d = 16n + lane%16) the 4 tokens 4*(lane/16) .. of that dim
-// (8 bytes; each instruction reads four full 128-byte lines).
+// 16-bit: K sub-tile [d/32][R][4][8] -> load m gives lane (t = lane%16) the
+// 8 dims 8*(4m + lane/16) .. of its token (16 bytes; each instruction reads
+// 1 KiB contiguous); V tile [b/4][d][4] -> load n gives lane
+// (d = 16n + lane%16) the 4 tokens 4*(lane/16) .. of that dim (8 bytes; each
+// instruction reads four full 128-byte lines).
 template <class Tag, int D, bool H = Is16<Tag>::value> struct Frag;
 
 // Each tile is read through its own buffer resource (base = tile address,
@@ -121,10 +122,10 @@ template <class Tag, int D> struct Frag<Tag, D, true> {
   u32x4 k[NK];
   u32x2 v[NV];
   template <int Pol = kKvCachePolicy>
-  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane, int = kRows) {
-    const int kr = (lane & 15) * (D * 2) + (lane >> 4) * 16;
+  __device__ inline void load(rsrc_t rk, rsrc_t rv, int lane, int rows = kRows) {
+    const int kr = (lane & 15) * 64 + (lane >> 4) * 16;
 #pragma unroll
-    for (int m = 0; m < NK; ++m) k[m] = buf_load16<Pol>(rk, kr + m * 64);
+    for (int m = 0; m < NK; ++m) k[m] = buf_load16<Pol>(rk, kr + m * rows * 64);
     const int vr = (lane >> 4) * (D * 8) + (lane & 15) * 8;
 #pragma unroll
     for (int n = 0; n < NV; ++n) v[n] = buf_load8<Pol>(rv, vr + n * 128);

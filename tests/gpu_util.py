@@ -47,27 +47,36 @@ def _fp8_tile_index(b: int, D: int):
     return k, v
 
 
-def pool_logical(kv, num_kv_heads: int, head_dim: int):
-    """Device pools -> fp64 CPU arrays [blocks][offset][head][dim], read through the
-    pool layout of include/pa.h (K tiles [b][d]; V tiles [b/4][d][4]; FP8 tiles
-    in their own permuted layout, returned as codes with the NaN codes as NaN)."""
+def pool_logical(kv, num_kv_heads: int, head_dim: int, host: bool = False):
+    """Device (or host swap) pools -> fp64 CPU arrays [blocks][offset][head][dim],
+    read through the pool layout of include/pa.h (16-bit K sub-tiles
+    [d/32][R][4][8], fp32 K tiles [b][d]; V tiles [b/4][d][4]; FP8 tiles in
+    their own permuted layout, returned as codes with the NaN codes as NaN)."""
+    kp, vp = (kv.host_k, kv.host_v) if host else (kv.k, kv.v)
+    kp, vp = kp.cpu(), vp.cpu()
+    b = kv.block_size
+    nb = kp.numel() // (num_kv_heads * b * head_dim)
     if kv.dtype == "fp8":
-        b = kv.block_size
-        nb = kv.k.numel() // (num_kv_heads * b * head_dim)
         ki, vi = _fp8_tile_index(b, head_dim)
-        kt = kv.k.view(nb, num_kv_heads, b * head_dim).cpu().numpy()
-        vt = kv.v.view(nb, num_kv_heads, b * head_dim).cpu().numpy()
+        kt = kp.view(nb, num_kv_heads, b * head_dim).numpy()
+        vt = vp.view(nb, num_kv_heads, b * head_dim).numpy()
         k = kt[:, :, ki].transpose(0, 2, 1, 3).astype(np.float64)     # [nb][b][H][D]
         v = vt[:, :, vi].transpose(0, 2, 1, 3).astype(np.float64)
         for a in (k, v):
             a[(a == 0x7F) | (a == 0xFF)] = np.nan
         return k, v
-    b = kv.block_size
-    nb = kv.k.numel() // (num_kv_heads * b * head_dim)
-    k = kv.k.view(nb, num_kv_heads, b, head_dim).permute(0, 2, 1, 3)
-    v = kv.v.view(nb, num_kv_heads, b // 4, head_dim, 4).permute(0, 2, 4, 1, 3)
+    if kv.dtype in ("bf16", "f16"):             # K sub-tiles [d/32][R][4][8], R = min(b, 16)
+        R = min(b, 16)
+        t = np.arange(b)[:, None]
+        d = np.arange(head_dim)[None, :]
+        idx = (t // R) * R * head_dim + (d // 32) * (R * 32) + (t % R) * 32 + d % 32
+        kt = kp.view(nb, num_kv_heads, b * head_dim)[:, :, torch.from_numpy(idx.ravel())]
+        k = kt.reshape(nb, num_kv_heads, b, head_dim).permute(0, 2, 1, 3)
+    else:
+        k = kp.view(nb, num_kv_heads, b, head_dim).permute(0, 2, 1, 3)
+    v = vp.view(nb, num_kv_heads, b // 4, head_dim, 4).permute(0, 2, 4, 1, 3)
     v = v.reshape(nb, b, num_kv_heads, head_dim)
-    return (k.to(torch.float64).cpu().numpy(), v.to(torch.float64).cpu().numpy())
+    return k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
 
 
 def assert_pool_equal(got: np.ndarray, want: np.ndarray) -> None:

@@ -28,15 +28,6 @@ def _gpu(request):
     torch.cuda.synchronize()
 
 
-def _host_logical(kv, Hkv, D):
-    """Host pools -> fp64 [blocks][offset][head][dim] through the pool layout."""
-    b = kv.block_size
-    nb = kv.host_blocks
-    k = kv.host_k.view(nb, Hkv, b, D).permute(0, 2, 1, 3)
-    v = kv.host_v.view(nb, Hkv, b // 4, D, 4).permute(0, 2, 4, 1, 3).reshape(nb, b, Hkv, D)
-    return k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
-
-
 def _oracle_host(run, Hkv, D):
     w = run.w
     shape = (w.host_blocks, w.block_size, Hkv, D)
@@ -70,7 +61,7 @@ def test_swap_script_pools_and_decode(name):
     got_k, got_v = pool_logical(batch.kv, w.num_kv_heads, w.head_dim)
     assert_pool_equal(got_k, want_k)
     assert_pool_equal(got_v, want_v)
-    hk, hv = _host_logical(batch.kv, w.num_kv_heads, w.head_dim)
+    hk, hv = pool_logical(batch.kv, w.num_kv_heads, w.head_dim, host=True)
     ok, ov = _oracle_host(run, w.num_kv_heads, w.head_dim)
     assert_pool_equal(hk, ok)
     assert_pool_equal(hv, ov)
