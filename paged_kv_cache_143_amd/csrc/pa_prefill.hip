@@ -18,9 +18,10 @@
 // heads of the group.  A wavefront owns NQ column groups and walks the
 // sequence's 16-token sub-tiles from position 0 up to its last row's
 // position, with the same registers-only pipeline as decode: K and V
-// fragments loaded straight from the pool layout one sub-tile ahead,
-// S^T = K q^T on the matrix cores, a causal mask per column, online softmax,
-// O^T += V^T P^T with P split into high and low 16-bit halves.  Each K/V
+// fragments loaded straight from the pool layout one step ahead (a step is
+// two sub-tiles for 16-bit pools, one for FP8 and fp32), S^T = K q^T on the
+// matrix cores, a causal mask per column, online softmax, O^T += V^T P^T
+// with P split into high and low 16-bit halves.  Each K/V
 // fragment serves NQ groups; the four wavefronts of a workgroup take
 // consecutive row ranges of one (sequence, KV head) and re-read the same
 // tiles, which the L2 serves (cached loads, unlike decode's streaming ones).
@@ -30,6 +31,127 @@
 #include "pa_tile.h"
 
 namespace pa {
+
+// ---- two sub-tiles per step (multi-token queries, 16-bit storage) ----------
+// 32 keys per step: the P.V product's k dimension holds 4 tokens of each
+// sub-tile per lane group (k slots 0..3: sub-tile a, 4..7: sub-tile b), so
+// the V operand is two 8-byte loads side by side -- no duplicated V -- and
+// the high and low 16-bit parts of P are two products with the same V.  The
+// masks for stored-length tails and causal limits run only on partial
+// steps; P is narrowed two values per conversion.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <class Tag> __device__ inline uint32_t pack2(f32x2 x);
+template <> __device__ inline uint32_t pack2<TagBF16>(f32x2 x) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+template <> __device__ inline uint32_t pack2<TagF16>(f32x2 x) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+}
+template <class Tag> __device__ inline f32x2 unpack2(uint32_t w);
+template <> __device__ inline f32x2 unpack2<TagBF16>(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(bf16x2, w), f32x2);
+}
+template <> __device__ inline f32x2 unpack2<TagF16>(uint32_t w) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
+
+template <class Tag, int D> struct FragPair {
+  u32x4 k[2][D / 32];     // K of sub-tiles a and b (the Frag<Tag> lane roles)
+  u32x4 v[D / 16];        // dim tile n: .xy = sub-tile a's 4 tokens, .zw = b's
+  template <int Pol = kKvCachePolicy>
+  __device__ inline void load(rsrc_t rka, rsrc_t rva, rsrc_t rkb, rsrc_t rvb, int lane,
+                              int rows) {
+    const int kr = (lane & 15) * 64 + (lane >> 4) * 16;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      k[0][m] = buf_load16<Pol>(rka, kr + m * rows * 64);
+      k[1][m] = buf_load16<Pol>(rkb, kr + m * rows * 64);
+    }
+    const int vr = (lane >> 4) * (D * 8) + (lane & 15) * 8;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const u32x2 a = buf_load8<Pol>(rva, vr + n * 128);
+      const u32x2 b = buf_load8<Pol>(rvb, vr + n * 128);
+      v[n] = u32x4{a[0], a[1], b[0], b[1]};
+    }
+  }
+};
+
+// nva, nvb: stored tokens of the two sub-tiles (0 for none); lima, limb: per
+// lane, the column's causal limit in rows of each sub-tile (>= 16: all visible).
+template <class Tag, int D>
+__device__ inline void attend_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& qf,
+                                   State<D>& st, int nva, int nvb, float qk_scale, int lane,
+                                   int lima, int limb) {
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    sa = mma32<Tag>(f.k[0][m], qf.q[m], sa);
+    sb = mma32<Tag>(f.k[1][m], qf.q[m], sb);
+  }
+  float x[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = sa[r] * qk_scale;
+    x[4 + r] = sb[r] * qk_scale;
+  }
+  const int t0 = 4 * (lane >> 4);
+  const bool partial =
+      nva < kRows || nvb < kRows || __builtin_amdgcn_ballot_w64(lima < kRows || limb < kRows) != 0;
+  u32x4 vm[D / 16];
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) vm[n] = f.v[n];
+  if (partial) {
+    uint32_t keep[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // select, never multiply: tails may hold NaN
+      if (t0 + r >= nva || t0 + r >= lima) x[r] = -INFINITY;
+      if (t0 + r >= nvb || t0 + r >= limb) x[4 + r] = -INFINITY;
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      keep[w] = (t0 + 2 * w < nva ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nva ? 0xffff0000u : 0u);
+      keep[2 + w] = (t0 + 2 * w < nvb ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nvb ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vm[n][e] &= keep[e];
+  }
+  bool over = false;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) over |= x[r] > st.m + kRescaleLog2;
+  if (__builtin_amdgcn_ballot_w64(over) != 0) {
+    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    bm = xor_max(bm);
+    const float m_new = fmaxf(st.m, bm);
+    const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.f : m_new));
+    st.l *= alpha;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) st.acc[n] *= alpha;
+    st.m = m_new;
+  }
+  const float base = st.m == -INFINITY ? 0.f : st.m;
+  float p[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) p[r] = fast_exp2(x[r] - base);
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  u32x4 hi, lo;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x2 pw = {p[2 * w], p[2 * w + 1]};
+    hi[w] = pack2<Tag>(pw);
+    lo[w] = pack2<Tag>(pw - unpack2<Tag>(hi[w]));
+  }
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(vm[n], hi, st.acc[n]);
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(vm[n], lo, st.acc[n]);
+}
 
 constexpr int kPWaves = 4;
 constexpr int kPThreads = kWave * kPWaves;
@@ -135,43 +257,86 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const int64_t block_stride = (int64_t)a.num_kv_heads * tile_bytes;
   const int cnt = p_last >= 0 ? p_last / a.rows + 1 : 0;    // sub-tiles to walk
 
-  Frag<Tag, D> fa, fb;
-  int nva = 0, nvb = 0;
   int c0 = 0, nc = 0, tb = 0;
-  auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
+  // Sub-tile i of the current chunk: its physical tile offset and stored-token
+  // count (0 past the walk or for a table entry outside the pool, whose
+  // resource then has size 0 and reads zeros).
+  auto locate = [&](int i, int64_t& off, int& bytes, int& nv) {
     int phys = __builtin_amdgcn_readlane(tb, min(i, nc - 1));
     const int j = c0 + i;
     const bool ok = i < nc && phys >= 0 && phys < a.num_blocks;
     nv = ok ? min(a.rows, L - j * a.rows) : 0;
     if (!ok) phys = 0;
-    const int64_t off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
-    const int bytes = ok ? sub_bytes : 0;
-    f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
-                                   tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
+    off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
+    bytes = ok ? sub_bytes : 0;
   };
-  using CT = typename ComputeTag<Tag>::type;
-  auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
-    if (nv <= 0) return;
-    const int key0 = (c0 + i) * a.rows;
-    const Frag<CT, D> w = compute_regs(f);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      attend_block<CT, D>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
-  };
-  auto open_chunk = [&]() {
+  auto open_table = [&]() {
     nc = min(kWave, cnt - c0);
     tb = lane < nc ? trow[(c0 + lane) / a.sub] : 0;
-    load_into(fa, 0, nva);
   };
 
-  for (; c0 < cnt; c0 += kWave) {
-    open_chunk();
-    for (int i = 0; i < nc; i += 2) {
-      load_into(fb, i + 1, nvb);
-      attend(fa, nva, i);
-      if (i + 1 >= nc) break;
-      load_into(fa, i + 2, nva);
-      attend(fb, nvb, i + 1);
+  if constexpr (Is16<Tag>::value && !IsFP8<Tag>::value) {
+    // Two sub-tiles per step, two steps in registers (one ahead).
+    FragPair<Tag, D> fa, fb;
+    int nva[2] = {0, 0}, nvb[2] = {0, 0};
+    auto load_pair = [&](FragPair<Tag, D>& f, int i, int* nv) {
+      int64_t oa, ob;
+      int ba, bb;
+      locate(2 * i, oa, ba, nv[0]);
+      locate(2 * i + 1, ob, bb, nv[1]);
+      f.template load<kPolicyCached>(tile_rsrc(a.k_pool + oa, ba), tile_rsrc(a.v_pool + oa, ba),
+                                     tile_rsrc(a.k_pool + ob, bb), tile_rsrc(a.v_pool + ob, bb),
+                                     lane, a.rows);
+    };
+    auto attend = [&](const FragPair<Tag, D>& f, const int* nv, int i) {
+      if (nv[0] <= 0) return;
+      const int key0 = (c0 + 2 * i) * a.rows;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        attend_pair<Tag, D>(f, qf[q], st[q], nv[0], nv[1], qk_scale, lane, pos[q] - key0 + 1,
+                            pos[q] - key0 - a.rows + 1);
+    };
+    for (; c0 < cnt; c0 += kWave) {
+      open_table();
+      const int np = (nc + 1) / 2;
+      load_pair(fa, 0, nva);
+      for (int i = 0; i < np; i += 2) {
+        load_pair(fb, i + 1, nvb);
+        attend(fa, nva, i);
+        if (i + 1 >= np) break;
+        load_pair(fa, i + 2, nva);
+        attend(fb, nvb, i + 1);
+      }
+    }
+  } else {
+    Frag<Tag, D> fa, fb;
+    int nva = 0, nvb = 0;
+    auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
+      int64_t off;
+      int bytes;
+      locate(i, off, bytes, nv);
+      f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
+                                     tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
+    };
+    using CT = typename ComputeTag<Tag>::type;
+    auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
+      if (nv <= 0) return;
+      const int key0 = (c0 + i) * a.rows;
+      const Frag<CT, D> w = compute_regs(f);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        attend_block<CT, D>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
+    };
+    for (; c0 < cnt; c0 += kWave) {
+      open_table();
+      load_into(fa, 0, nva);
+      for (int i = 0; i < nc; i += 2) {
+        load_into(fb, i + 1, nvb);
+        attend(fa, nva, i);
+        if (i + 1 >= nc) break;
+        load_into(fa, i + 2, nva);
+        attend(fb, nvb, i + 1);
+      }
     }
   }
 
