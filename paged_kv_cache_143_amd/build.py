@@ -17,10 +17,15 @@ LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_cache.hip", "pa_decode.hip", "pa_prefill.hip"]
 ARCH = "gfx950"
 
-# Packed fp32 instructions are disabled for all device code.
+# Packed fp32 instructions are disabled for all device code.  Matrix-core
+# results and accumulators are kept in VGPRs (the AGPR file then holds operand
+# fragments): the prefill loop rescales its accumulators with VALU code, which
+# otherwise makes the compiler copy every accumulator out of the AGPR file on
+# every step.  Decode and cache kernels compile to the same code either way.
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-result",
 ]
 

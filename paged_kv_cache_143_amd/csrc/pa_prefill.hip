@@ -79,8 +79,27 @@ template <class Tag, int D> struct FragPair {
   }
 };
 
+// Zero the V tokens at and past each sub-tile's stored count, in place (a
+// tail may hold NaN, and 0 * NaN would reach the accumulators).  The masks
+// depend on the stored counts only, so one pass serves every column group.
+template <class Tag, int D>
+__device__ inline void mask_v_tails(FragPair<Tag, D>& f, int nva, int nvb, int lane) {
+  const int t0 = 4 * (lane >> 4);
+  uint32_t keep[4];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    keep[w] = (t0 + 2 * w < nva ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nva ? 0xffff0000u : 0u);
+    keep[2 + w] = (t0 + 2 * w < nvb ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nvb ? 0xffff0000u : 0u);
+  }
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[n][e] &= keep[e];
+}
+
 // nva, nvb: stored tokens of the two sub-tiles (0 for none); lima, limb: per
-// lane, the column's causal limit in rows of each sub-tile (>= 16: all visible).
+// lane, the column's causal limit in rows of each sub-tile (>= 16: all
+// visible).  V tails must already be masked (mask_v_tails).
 template <class Tag, int D>
 __device__ inline void attend_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& qf,
                                    State<D>& st, int nva, int nvb, float qk_scale, int lane,
@@ -97,29 +116,16 @@ __device__ inline void attend_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D
     x[r] = sa[r] * qk_scale;
     x[4 + r] = sb[r] * qk_scale;
   }
-  const int t0 = 4 * (lane >> 4);
-  const bool partial =
-      nva < kRows || nvb < kRows || __builtin_amdgcn_ballot_w64(lima < kRows || limb < kRows) != 0;
-  u32x4 vm[D / 16];
-#pragma unroll
-  for (int n = 0; n < D / 16; ++n) vm[n] = f.v[n];
-  if (partial) {
-    uint32_t keep[4];
+  if (nva < kRows || nvb < kRows ||
+      __builtin_amdgcn_ballot_w64(lima < kRows || limb < kRows) != 0) {
+    const int t0 = 4 * (lane >> 4);
+    const int ea = min(nva, lima), eb = min(nvb, limb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       // select, never multiply: tails may hold NaN
-      if (t0 + r >= nva || t0 + r >= lima) x[r] = -INFINITY;
-      if (t0 + r >= nvb || t0 + r >= limb) x[4 + r] = -INFINITY;
+      if (t0 + r >= ea) x[r] = -INFINITY;
+      if (t0 + r >= eb) x[4 + r] = -INFINITY;
     }
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      keep[w] = (t0 + 2 * w < nva ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nva ? 0xffff0000u : 0u);
-      keep[2 + w] = (t0 + 2 * w < nvb ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nvb ? 0xffff0000u : 0u);
-    }
-#pragma unroll
-    for (int n = 0; n < D / 16; ++n)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vm[n][e] &= keep[e];
   }
   bool over = false;
 #pragma unroll
@@ -148,9 +154,9 @@ __device__ inline void attend_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D
     lo[w] = pack2<Tag>(pw - unpack2<Tag>(hi[w]));
   }
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(vm[n], hi, st.acc[n]);
+  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(f.v[n], hi, st.acc[n]);
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(vm[n], lo, st.acc[n]);
+  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(f.v[n], lo, st.acc[n]);
 }
 
 constexpr int kPWaves = 4;
@@ -288,8 +294,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
                                      tile_rsrc(a.k_pool + ob, bb), tile_rsrc(a.v_pool + ob, bb),
                                      lane, a.rows);
     };
-    auto attend = [&](const FragPair<Tag, D>& f, const int* nv, int i) {
+    auto attend = [&](FragPair<Tag, D>& f, const int* nv, int i) {
       if (nv[0] <= 0) return;
+      if (nv[0] < kRows || nv[1] < kRows) mask_v_tails(f, nv[0], nv[1], lane);
       const int key0 = (c0 + 2 * i) * a.rows;
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
