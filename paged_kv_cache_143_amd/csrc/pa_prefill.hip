@@ -17,15 +17,19 @@
 // pair; a 16-column group packs floor(16 / G) consecutive rows times the G
 // heads of the group.  A wavefront owns NQ column groups and walks the
 // sequence's 16-token sub-tiles from position 0 up to its last row's
-// position, with the same registers-only pipeline as decode: K and V
-// fragments loaded straight from the pool layout one step ahead (a step is
-// two sub-tiles for 16-bit pools, one for FP8 and fp32), S^T = K q^T on the
-// matrix cores, a causal mask per column, online softmax, O^T += V^T P^T
-// with P split into high and low 16-bit halves.  Each K/V
-// fragment serves NQ groups; the four wavefronts of a workgroup take
+// position: S^T = K q^T on the matrix cores, a causal mask per column, online
+// softmax, O^T += V^T P^T with P split into high and low 16-bit halves.  Each
+// K/V fragment serves NQ groups; the four wavefronts of a workgroup take
 // consecutive row ranges of one (sequence, KV head) and re-read the same
-// tiles, which the L2 serves (cached loads, unlike decode's streaming ones).
-// Workgroups run the chunk's last rows (the most keys) first.
+// tiles, which the L1 and L2 serve (cached loads, unlike decode's streaming
+// ones).  For 16-bit pools a step is two sub-tiles held in one register
+// buffer that is refilled in phases (the next K once this step's S^T products
+// are issued, the next V once its P.V products are), which keeps the kernel
+// under 256 registers: two wavefronts per SIMD.  Sub-tile addresses are built
+// 64 at a time, one per lane, and broadcast per step.  FP8 and fp32 pools take
+// one sub-tile per step with a second buffer one step ahead.  Each XCD runs
+// the row tiles of one (sequence, KV head) after another, last rows (the most
+// keys) first, so its resident workgroups share K/V in its L2.
 #include <algorithm>
 
 #include "pa_tile.h"
@@ -57,24 +61,34 @@ template <> __device__ inline f32x2 unpack2<TagF16>(uint32_t w) {
   return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
 }
 
+typedef const __attribute__((address_space(1))) char* gchar;
+
 template <class Tag, int D> struct FragPair {
   u32x4 k[2][D / 32];     // K of sub-tiles a and b (the Frag<Tag> lane roles)
   u32x4 v[D / 16];        // dim tile n: .xy = sub-tile a's 4 tokens, .zw = b's
-  template <int Pol = kKvCachePolicy>
-  __device__ inline void load(rsrc_t rka, rsrc_t rva, rsrc_t rkb, rsrc_t rvb, int lane,
-                              int rows) {
-    const int kr = (lane & 15) * 64 + (lane >> 4) * 16;
+  // ka, kb: the two K sub-tiles (wave-uniform); kro[m]: this lane's byte
+  // offset of K dims 32m.. (rows-dependent).  Plain cached global loads.
+  __device__ inline void load_k(gchar ka, gchar kb, const uint32_t* kro) {
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
-      k[0][m] = buf_load16<Pol>(rka, kr + m * rows * 64);
-      k[1][m] = buf_load16<Pol>(rkb, kr + m * rows * 64);
+      // The empty statement pins the 32-bit offset here, so the address stays
+      // "uniform base + zero-extended lane offset" (one load, no 64-bit adds)
+      // instead of a hoisted 64-bit per-lane value.
+      uint32_t o = kro[m];
+      asm volatile("" : "+v"(o));
+      k[0][m] = *(const __attribute__((address_space(1))) u32x4*)(ka + o);
+      k[1][m] = *(const __attribute__((address_space(1))) u32x4*)(kb + o);
     }
-    const int vr = (lane >> 4) * (D * 8) + (lane & 15) * 8;
+  }
+  // va, vb: the two V sub-tiles; vr: this lane's byte offset of V dim-tile 0
+  // (tile n adds 128 n).
+  __device__ inline void load_v(gchar va, gchar vb, uint32_t vr) {
+    asm volatile("" : "+v"(vr));
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
-      const u32x2 a = buf_load8<Pol>(rva, vr + n * 128);
-      const u32x2 b = buf_load8<Pol>(rvb, vr + n * 128);
-      v[n] = u32x4{a[0], a[1], b[0], b[1]};
+      const u32x2 x = *(const __attribute__((address_space(1))) u32x2*)(va + vr + n * 128);
+      const u32x2 y = *(const __attribute__((address_space(1))) u32x2*)(vb + vr + n * 128);
+      v[n] = u32x4{x[0], x[1], y[0], y[1]};
     }
   }
 };
@@ -97,19 +111,27 @@ __device__ inline void mask_v_tails(FragPair<Tag, D>& f, int nva, int nvb, int l
     for (int e = 0; e < 4; ++e) f.v[n][e] &= keep[e];
 }
 
-// nva, nvb: stored tokens of the two sub-tiles (0 for none); lima, limb: per
-// lane, the column's causal limit in rows of each sub-tile (>= 16: all
-// visible).  V tails must already be masked (mask_v_tails).
+// S^T of the pair's two sub-tiles for one column group.
 template <class Tag, int D>
-__device__ inline void attend_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& qf,
-                                   State<D>& st, int nva, int nvb, float qk_scale, int lane,
-                                   int lima, int limb) {
-  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+__device__ inline void qk_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& qf, f32x4& sa,
+                               f32x4& sb) {
+  sa = f32x4{0.f, 0.f, 0.f, 0.f};
+  sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
     sa = mma32<Tag>(f.k[0][m], qf.q[m], sa);
     sb = mma32<Tag>(f.k[1][m], qf.q[m], sb);
   }
+}
+
+// Online softmax and O^T += V^T P^T for one column group, from its scores.
+// nva, nvb: stored tokens of the two sub-tiles (0 for none); lima, limb: per
+// lane, the column's causal limit in rows of each sub-tile (>= 16: all
+// visible).  V tails must already be masked (mask_v_tails).
+template <class Tag, int D>
+__device__ inline void softmax_pv(const FragPair<Tag, D>& f, f32x4 sa, f32x4 sb, State<D>& st,
+                                  int nva, int nvb, float qk_scale, int lane, int lima,
+                                  int limb) {
   float x[8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -161,6 +183,7 @@ __device__ inline void attend_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D
 
 constexpr int kPWaves = 4;
 constexpr int kPThreads = kWave * kPWaves;
+constexpr int kXcds = 8;     // accelerator complex dies of one MI355X
 
 #ifndef PA_PREFILL_NQ
 #define PA_PREFILL_NQ 2
@@ -199,11 +222,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-  const int unit = blockIdx.x;
-  const int g = unit % a.num_kv_heads;
-  const int rest = unit / a.num_kv_heads;
-  const int seq = rest % a.num_seqs;
-  const int tile = a.num_tiles - 1 - rest / a.num_seqs;
+  // Workgroup order.  The dispatcher places workgroup i on XCD i % kXcds,
+  // each XCD with its own L2.  XCD x takes (sequence, KV head) pairs x,
+  // x + kXcds, ... and runs all row tiles of one pair (last rows, the most
+  // keys, first) before the next, so its resident workgroups share one or two
+  // K/V prefixes in its L2; with kXcds KV heads every XCD holds one head of
+  // every sequence, which also balances their work.
+  const int xcd = blockIdx.x % kXcds;
+  const int k = blockIdx.x / kXcds;
+  const int pair = xcd + kXcds * (k / a.num_tiles);
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int seq = pair / a.num_kv_heads;
+  const int g = pair - seq * a.num_kv_heads;
+  const int tile = a.num_tiles - 1 - k % a.num_tiles;
 
   const int qs = a.q_start[seq];
   const int n = a.q_start[seq + 1] - qs;
@@ -282,38 +313,78 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   };
 
   if constexpr (Is16<Tag>::value && !IsFP8<Tag>::value) {
-    // Two sub-tiles per step, two steps in registers (one ahead).
-    FragPair<Tag, D> fa, fb;
-    int nva[2] = {0, 0}, nvb[2] = {0, 0};
-    auto load_pair = [&](FragPair<Tag, D>& f, int i, int* nv) {
-      int64_t oa, ob;
-      int ba, bb;
-      locate(2 * i, oa, ba, nv[0]);
-      locate(2 * i + 1, ob, bb, nv[1]);
-      f.template load<kPolicyCached>(tile_rsrc(a.k_pool + oa, ba), tile_rsrc(a.v_pool + oa, ba),
-                                     tile_rsrc(a.k_pool + ob, bb), tile_rsrc(a.v_pool + ob, bb),
-                                     lane, a.rows);
+    // Two sub-tiles per step, two steps in registers (one ahead).  Sub-tile
+    // descriptors are built 64 at a time, one per lane (K address and stored
+    // count), and read with lane broadcasts; a pair never straddles two sets.
+    // Sub-tiles past the walk or behind a table entry outside the pool get
+    // count 0 and the address of block 0's tile (in bounds: a pool holds at
+    // least one block), so every load is valid and the masks drop them.
+    const uint64_t k_base = (uint64_t)a.k_pool;
+    const uint64_t v_delta = (uint64_t)a.v_pool - k_base;
+    uint32_t d_lo = 0, d_hi = 0;
+    int d_nv = 0, dbase = -kWave;
+    auto open_set = [&](int first) {
+      const int j = first + lane;
+      const int phys = j < cnt ? trow[j / a.sub] : -1;
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      d_nv = ok ? min(a.rows, L - j * a.rows) : 0;
+      const uint64_t addr = k_base + (uint64_t)(ok ? phys : 0) * (uint64_t)block_stride +
+                            (uint64_t)head_tile + (uint64_t)(j % a.sub) * (uint64_t)sub_bytes;
+      d_lo = (uint32_t)addr;
+      d_hi = (uint32_t)(addr >> 32);
     };
-    auto attend = [&](FragPair<Tag, D>& f, const int* nv, int i) {
-      if (nv[0] <= 0) return;
-      if (nv[0] < kRows || nv[1] < kRows) mask_v_tails(f, nv[0], nv[1], lane);
-      const int key0 = (c0 + 2 * i) * a.rows;
+    uint32_t kro[D / 32];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        attend_pair<Tag, D>(f, qf[q], st[q], nv[0], nv[1], qk_scale, lane, pos[q] - key0 + 1,
-                            pos[q] - key0 - a.rows + 1);
-    };
-    for (; c0 < cnt; c0 += kWave) {
-      open_table();
-      const int np = (nc + 1) / 2;
-      load_pair(fa, 0, nva);
-      for (int i = 0; i < np; i += 2) {
-        load_pair(fb, i + 1, nvb);
-        attend(fa, nva, i);
-        if (i + 1 >= np) break;
-        load_pair(fa, i + 2, nva);
-        attend(fb, nvb, i + 1);
+    for (int m = 0; m < D / 32; ++m)
+      kro[m] = (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16 + m * a.rows * 64);
+    const uint32_t vro = (uint32_t)((lane >> 4) * (D * 8) + (lane & 15) * 8);
+
+    // One fragment buffer, refilled in phases: the next pair's K as soon as
+    // this pair's S^T products are issued, its V once the P.V products are.
+    FragPair<Tag, D> f;
+    int nv[2] = {0, 0};
+    uint64_t ka = 0, kb = 0;
+    auto locate_pair = [&](int P, int* n2) {
+      const int s0 = 2 * P;
+      if (s0 - dbase >= kWave) {
+        dbase += kWave;
+        open_set(dbase);
       }
+      const int i = s0 - dbase;
+      ka = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(d_hi, i) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane(d_lo, i);
+      kb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(d_hi, i + 1) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane(d_lo, i + 1);
+      n2[0] = __builtin_amdgcn_readlane(d_nv, i);
+      n2[1] = __builtin_amdgcn_readlane(d_nv, i + 1);
+    };
+    const int np = (cnt + 1) / 2;
+    if (np > 0) {
+      locate_pair(0, nv);
+      f.load_k((gchar)ka, (gchar)kb, kro);
+      f.load_v((gchar)(ka + v_delta), (gchar)(kb + v_delta), vro);
+    }
+    for (int P = 0; P < np; ++P) {
+      const bool more = P + 1 < np;
+      int nn[2] = {0, 0};
+      f32x4 sa[NQ], sb[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], sa[q], sb[q]);
+      if (more) {
+        locate_pair(P + 1, nn);
+        f.load_k((gchar)ka, (gchar)kb, kro);
+      }
+      if (nv[0] > 0 || nv[1] > 0) {
+        if (nv[0] < kRows || nv[1] < kRows) mask_v_tails(f, nv[0], nv[1], lane);
+        const int key0 = 2 * P * a.rows;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          softmax_pv<Tag, D>(f, sa[q], sb[q], st[q], nv[0], nv[1], qk_scale, lane,
+                             pos[q] - key0 + 1, pos[q] - key0 - a.rows + 1);
+      }
+      if (more) f.load_v((gchar)(ka + v_delta), (gchar)(kb + v_delta), vro);
+      nv[0] = nn[0];
+      nv[1] = nn[1];
     }
   } else {
     Frag<Tag, D> fa, fb;
@@ -429,7 +500,8 @@ pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_pool, con
   a.qk_scale = scale * 1.4426950408889634f;
   a.k_scales = pool->k_scales;
   a.v_scales = pool->v_scales;
-  const int64_t units = (int64_t)a.num_kv_heads * num_seqs * a.num_tiles;
+  const int64_t pairs = (int64_t)a.num_kv_heads * num_seqs;
+  const int64_t units = (pairs + kXcds - 1) / kXcds * kXcds * a.num_tiles;
   if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
   const int D = pool->head_dim;

@@ -128,3 +128,36 @@ def test_full_size_sampled(make, picks):
     err = row_rel_err(got[idx], ref)
     announce(f"{w.name}: sampled rows max rel err {err:.3e}")
     assert err <= 2e-3
+
+
+@pytest.mark.parametrize("b,bad", [(16, 2), (16, 3), (32, 1), (8, 4), (8, 5)])
+def test_out_of_pool_entry_contributes_nothing(b, bad):
+    """A table entry outside the pool drops that block's tokens from the softmax
+    and nothing else: rows of the same sequence still see every other key
+    (including the other sub-tile processed in the same step), at unchanged
+    positions; other sequences are untouched."""
+    from paged_kv_cache_143_amd import binding as B
+    w = W.chunked("pbad", 104, "bf16", [90, 70, 40], [30, 45, 60], 16, 4, 128, block_size=b)
+    _, batch, step = _run(w)
+    tab = batch.tables.clone()
+    tab[1, bad] = w.num_blocks + 7
+    out = torch.full_like(step.out, 7.0)
+    B.prefill_attention_t(batch.kv.desc, batch.kv.k, batch.kv.v, step.q, out, step.q_start, tab,
+                          batch.lens, w.scale, step.max_chunk, batch.max_len)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    run = OracleRun(w)
+    ref = run.prefill()
+    starts = np.concatenate([[0], np.cumsum(w.chunk_lens)])
+    q = run.chunk_q64()
+    K, V = run.logical_kv(1)
+    L, n = K.shape[0], w.chunk_lens[1]
+    assert (bad + 1) * b <= L - n          # the dropped block lies in the cached prefix
+    for t in range(n):
+        p = L - n + t
+        keep = [k for k in range(p + 1) if not bad * b <= k < (bad + 1) * b]
+        ref[starts[1] + t] = OA.decode_sequence(q[starts[1] + t], K[keep], V[keep], w.scale)
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    announce(f"b={b} bad entry {bad}: max row rel err {err:.3e}")
+    assert err <= 2e-3
