@@ -476,22 +476,26 @@ void decode_kernel(DecodeArgs a) {
   using CT = typename ComputeTag<Tag>::type;
   Frag<Tag, D> f[NBuf];
   int nv[NBuf];
-  int c0 = 0, n = 0, tb = 0;
-  // Block i of the chunk: physical id (0 when out of range: loads stay in
-  // bounds and the block contributes nothing) and its valid-token count,
-  // negated for the block that holds the current token (patched first).
-  // i == n is the prefetch past the wavefront's last block: a size-0
-  // resource, like a table entry outside the pool.
+  int c0 = 0, n = 0;
+  // Per-lane descriptors of the chunk's blocks, lane i for block i: the K
+  // address of its sub-tile and its valid-token count (0 for a table entry
+  // outside the pool, negated for the block that holds the current token,
+  // which is patched first).  A block is then a lane broadcast, not address
+  // arithmetic.  Blocks past the wavefront's last one (the ring's prefetch)
+  // get count 0 and a size-0 resource: no memory access, static wait counts.
+  const uint64_t k_base = (uint64_t)a.k_pool;
+  const uint64_t v_delta = (uint64_t)a.v_pool - k_base;
+  const int sub_shift = a.sub >> 1;          // sub-tiles per block: 1 or 2
+  uint32_t d_lo = 0, d_hi = 0;
+  int d_nv = 0;
   auto load_into = [&](Frag<Tag, D>& fr, int i, int& nvr) {
-    int phys = __builtin_amdgcn_readlane(tb, min(i, n - 1));
-    const int j = first + kWaves * (c0 + i);
-    const bool ok = i < n && phys >= 0 && phys < a.num_blocks;
-    nvr = ok ? min(a.rows, L - j * a.rows) : 0;
-    if (!ok) phys = 0;
-    if (own_new && j == j_new) nvr = -nvr;
-    const int64_t off = (int64_t)phys * block_stride + head_tile + (int64_t)(j % a.sub) * sub_bytes;
-    const int bytes = ok ? sub_bytes : 0;
-    fr.load(tile_rsrc(a.k_pool + off, bytes), tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
+    const int li = min(i, kWave - 1);
+    nvr = i < n ? __builtin_amdgcn_readlane(d_nv, li) : 0;
+    const uint64_t ka = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(d_hi, li) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane(d_lo, li);
+    const int bytes = nvr != 0 ? sub_bytes : 0;
+    fr.load(tile_rsrc((const char*)ka, bytes), tile_rsrc((const char*)(ka + v_delta), bytes), lane,
+            a.rows);
   };
   auto attend_regs = [&](Frag<CT, D>& w, int nvr) {
     if (nvr < 0) {
@@ -510,7 +514,16 @@ void decode_kernel(DecodeArgs a) {
   };
   auto open_chunk = [&]() {
     n = min(kWave, cnt - c0);
-    tb = lane < n ? trow[(first + kWaves * (c0 + lane)) / a.sub] : 0;
+    const int j = first + kWaves * (c0 + lane);
+    const int phys = lane < n ? trow[j >> sub_shift] : -1;
+    const bool ok = phys >= 0 && phys < a.num_blocks;
+    int c = ok ? min(a.rows, L - j * a.rows) : 0;
+    if (own_new && j == j_new) c = -c;
+    d_nv = c;
+    const uint64_t addr = k_base + (uint64_t)(ok ? phys : 0) * (uint64_t)block_stride +
+                          (uint64_t)head_tile + (uint64_t)(j & (a.sub - 1)) * (uint64_t)sub_bytes;
+    d_lo = (uint32_t)addr;
+    d_hi = (uint32_t)(addr >> 32);
 #pragma unroll
     for (int u = 0; u + 1 < NBuf; ++u) load_into(f[u], u, nv[u]);
   };
