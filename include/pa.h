@@ -280,6 +280,8 @@ PA_API pa_status pa_decode_step(const pa_pool_desc* pool, void* k_pool, void* v_
  *   max_chunk_len  >= every n_i (host value; sizes the grid).  Rows of a
  *                  chunk past it are not computed.
  *   other arguments as pa_decode_attention (lengths clipped the same way).
+ * A table entry outside the pool contributes no tokens: its block drops out
+ * of every row's softmax and the other positions keep their places.
  * A row with p < 0 (n_i > L_i) gets zeros.  Accumulation is fp32; P is split
  * into high and low 16-bit parts for the P.V products as in decode.
  */
