@@ -384,6 +384,26 @@ template <class Tag, int D> struct WavesPerEU {
   static constexpr int value = (!Is16<Tag>::value && D == 128) ? 2 : PA_WAVES_PER_EU;
 };
 
+// 8-token blocks, 16-bit pools: two blocks fill one 16-row tile -- rows 0-7
+// from block a, rows 8-15 from block b (each lane's K pieces come from the
+// block of its row; V token groups 0-1 from a, 2-3 from b) -- with streaming
+// global loads from per-lane addresses, so one load instruction covers whole
+// lines of both blocks instead of half a tile.  ka, kb: the blocks' K tiles of
+// this KV head; their V tiles are v_delta further.
+template <class Tag, int D>
+__device__ inline void load_pair8(Frag<Tag, D, true>& f, uint64_t ka, uint64_t kb,
+                                  uint64_t v_delta, int lane) {
+  typedef const __attribute__((address_space(1))) u32x4* g16;
+  typedef const __attribute__((address_space(1))) u32x2* g8;
+  const uint64_t kl = ((lane & 15) < 8 ? ka : kb) + (uint32_t)((lane & 7) * 64 + (lane >> 4) * 16);
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) f.k[m] = __builtin_nontemporal_load((g16)(kl + m * 8 * 64));
+  const uint64_t vl = ((lane >> 4) < 2 ? ka : kb) + v_delta +
+                      (uint32_t)(((lane >> 4) & 1) * (D * 8) + (lane & 15) * 8);
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) f.v[n] = __builtin_nontemporal_load((g8)(vl + n * 128));
+}
+
 // Register buffers in the block ring: FP8 sub-tiles are half the bytes, so
 // two are kept in flight ahead of the one being computed.
 #ifndef PA_FP8_BUFS
@@ -391,7 +411,9 @@ template <class Tag, int D> struct WavesPerEU {
 #endif
 template <class Tag> struct RingBufs { static constexpr int value = IsFP8<Tag>::value ? PA_FP8_BUFS : 2; };
 
-template <class Tag, int D, class OutT>
+// P8: 8-token blocks of a 16-bit pool, walked as 16-token tiles of two blocks
+// (load_pair8); `rows` below is then 16 while a block holds 8.
+template <class Tag, int D, class OutT, bool P8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_kernel(DecodeArgs a) {
   constexpr int NBuf = RingBufs<Tag>::value;
@@ -433,10 +455,12 @@ void decode_kernel(DecodeArgs a) {
   }
   if (part >= n_parts) return;
 
-  // From here on j counts sub-tiles of `rows` tokens.
-  const int nsub_seq = (L + a.rows - 1) / a.rows;
-  const int j0 = part * (a.ps / a.rows);
-  const int j1 = min(nsub_seq, j0 + a.ps / a.rows);
+  // From here on j counts tiles of `rows` tokens (sub-tiles, or pairs of
+  // 8-token blocks when P8).
+  const int rows = P8 ? kRows : a.rows;
+  const int nsub_seq = (L + rows - 1) / rows;
+  const int j0 = part * (a.ps / rows);
+  const int j1 = min(nsub_seq, j0 + a.ps / rows);
   const int first = j0 + wave;
   const int cnt = first < j1 ? (j1 - first + kWaves - 1) / kWaves : 0;
 
@@ -464,9 +488,13 @@ void decode_kernel(DecodeArgs a) {
   const int64_t block_stride = (int64_t)a.num_kv_heads * tile_bytes;
 
   // Fused step: the unit holding position L-1 writes the current token.
-  const int j_new = (L - 1) / a.rows;          // its sub-tile
-  const int o_new = (L - 1) % a.rows;          // its register row
+  const int j_new = (L - 1) / rows;            // its tile
+  int o_new = (L - 1) % rows;                  // its register row
   const bool own_new = a.k_new != nullptr && j_new >= j0 && j_new < j1;
+  if (P8 && own_new && o_new >= 8) {           // in block b: it moves up when block a is out
+    const int pa_ = trow[2 * j_new];          // of the pool (valid blocks are packed first)
+    if (pa_ < 0 || pa_ >= a.num_blocks) o_new -= 8;
+  }
   char* stage = reinterpret_cast<char*>(smem) + a.stage_off;
   NewToken<Tag, D> tok;
   if (own_new) tok.load(a, seq, g);             // in flight with the first blocks
@@ -486,16 +514,22 @@ void decode_kernel(DecodeArgs a) {
   const uint64_t k_base = (uint64_t)a.k_pool;
   const uint64_t v_delta = (uint64_t)a.v_pool - k_base;
   const int sub_shift = a.sub >> 1;          // sub-tiles per block: 1 or 2
-  uint32_t d_lo = 0, d_hi = 0;
+  uint32_t d_lo = 0, d_hi = 0, d_lo2 = 0, d_hi2 = 0;   // d_*2: block b when P8
   int d_nv = 0;
   auto load_into = [&](Frag<Tag, D>& fr, int i, int& nvr) {
     const int li = min(i, kWave - 1);
     nvr = i < n ? __builtin_amdgcn_readlane(d_nv, li) : 0;
     const uint64_t ka = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(d_hi, li) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane(d_lo, li);
-    const int bytes = nvr != 0 ? sub_bytes : 0;
-    fr.load(tile_rsrc((const char*)ka, bytes), tile_rsrc((const char*)(ka + v_delta), bytes), lane,
-            a.rows);
+    if constexpr (P8) {
+      const uint64_t kb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(d_hi2, li) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane(d_lo2, li);
+      load_pair8<Tag, D>(fr, ka, kb, v_delta, lane);
+    } else {
+      const int bytes = nvr != 0 ? sub_bytes : 0;
+      fr.load(tile_rsrc((const char*)ka, bytes), tile_rsrc((const char*)(ka + v_delta), bytes),
+              lane, a.rows);
+    }
   };
   auto attend_regs = [&](Frag<CT, D>& w, int nvr) {
     if (nvr < 0) {
@@ -515,15 +549,43 @@ void decode_kernel(DecodeArgs a) {
   auto open_chunk = [&]() {
     n = min(kWave, cnt - c0);
     const int j = first + kWaves * (c0 + lane);
-    const int phys = lane < n ? trow[j >> sub_shift] : -1;
-    const bool ok = phys >= 0 && phys < a.num_blocks;
-    int c = ok ? min(a.rows, L - j * a.rows) : 0;
-    if (own_new && j == j_new) c = -c;
-    d_nv = c;
-    const uint64_t addr = k_base + (uint64_t)(ok ? phys : 0) * (uint64_t)block_stride +
-                          (uint64_t)head_tile + (uint64_t)(j & (a.sub - 1)) * (uint64_t)sub_bytes;
-    d_lo = (uint32_t)addr;
-    d_hi = (uint32_t)(addr >> 32);
+    if constexpr (P8) {
+      // Blocks 2j and 2j+1.  Decode has no causal order, so valid blocks are
+      // packed first and the tile's valid rows stay a prefix: block a out of
+      // the pool -> block b takes rows 0-7.  Missing blocks, and tiles past
+      // the wavefront's last (the ring's prefetch), read block 0's tile of
+      // this head (in bounds; shared by every such read, so it stays cached)
+      // and are masked by the count.
+      const int pa_ = lane < n ? trow[2 * j] : -1;
+      const bool has_b = lane < n && (2 * j + 1) * 8 < L;
+      const int pb_ = has_b ? trow[2 * j + 1] : -1;
+      const bool oka = pa_ >= 0 && pa_ < a.num_blocks;
+      const bool okb = pb_ >= 0 && pb_ < a.num_blocks;
+      const int ca = oka ? min(8, L - 16 * j) : 0;
+      const int cb = okb ? min(8, L - 16 * j - 8) : 0;
+      int c = ca + cb;
+      if (own_new && j == j_new) c = -c;
+      d_nv = c;
+      const int first_blk = oka ? pa_ : (okb ? pb_ : 0);
+      const int second_blk = oka && okb ? pb_ : 0;
+      const uint64_t a0 = k_base + (uint64_t)head_tile;
+      const uint64_t aa = a0 + (uint64_t)first_blk * (uint64_t)block_stride;
+      const uint64_t ab = a0 + (uint64_t)second_blk * (uint64_t)block_stride;
+      d_lo = (uint32_t)aa;
+      d_hi = (uint32_t)(aa >> 32);
+      d_lo2 = (uint32_t)ab;
+      d_hi2 = (uint32_t)(ab >> 32);
+    } else {
+      const int phys = lane < n ? trow[j >> sub_shift] : -1;
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      int c = ok ? min(a.rows, L - j * a.rows) : 0;
+      if (own_new && j == j_new) c = -c;
+      d_nv = c;
+      const uint64_t addr = k_base + (uint64_t)(ok ? phys : 0) * (uint64_t)block_stride +
+                            (uint64_t)head_tile + (uint64_t)(j & (a.sub - 1)) * (uint64_t)sub_bytes;
+      d_lo = (uint32_t)addr;
+      d_hi = (uint32_t)(addr >> 32);
+    }
 #pragma unroll
     for (int u = 0; u + 1 < NBuf; ++u) load_into(f[u], u, nv[u]);
   };
@@ -648,9 +710,9 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   for (int e = 0; e < PER; ++e) store_out<OutT>(o + lane + e * kWave, den > 0.f ? num[e] / den : 0.f);
 }
 
-template <class Tag, int D, class OutT>
+template <class Tag, int D, class OutT, bool P8>
 static pa_status launch(const DecodeArgs& a, int64_t units, size_t lds, hipStream_t stream) {
-  decode_kernel<Tag, D, OutT><<<(unsigned)units, kThreads, lds, stream>>>(a);
+  decode_kernel<Tag, D, OutT, P8><<<(unsigned)units, kThreads, lds, stream>>>(a);
   pa_status st = launch_status();
   if (st != PA_OK || a.num_parts <= 1) return st;
   const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
@@ -658,10 +720,18 @@ static pa_status launch(const DecodeArgs& a, int64_t units, size_t lds, hipStrea
   return launch_status();
 }
 
-template <class Tag, class OutT>
+template <class Tag, class OutT, bool P8 = false>
 static pa_status dispatch_d(int D, const DecodeArgs& a, int64_t units, size_t lds, hipStream_t s) {
-  if (D == 128) return launch<Tag, 128, OutT>(a, units, lds, s);
-  return launch<Tag, 64, OutT>(a, units, lds, s);
+  if (D == 128) return launch<Tag, 128, OutT, P8>(a, units, lds, s);
+  return launch<Tag, 64, OutT, P8>(a, units, lds, s);
+}
+// 16-bit pools with 8-token blocks walk pairs of blocks (P8) whenever the
+// partitions hold whole pairs.
+template <class Tag, class OutT>
+static pa_status dispatch_16(bool p8, int D, const DecodeArgs& a, int64_t units, size_t lds,
+                             hipStream_t s) {
+  return p8 ? dispatch_d<Tag, OutT, true>(D, a, units, lds, s)
+            : dispatch_d<Tag, OutT, false>(D, a, units, lds, s);
 }
 
 // Partition geometry shared by the size query and the launch.
@@ -686,7 +756,9 @@ static int32_t auto_partition(int64_t base_units, int32_t max_len) {
 static void geometry(int32_t max_len, int32_t partition_size, int64_t base_units, int32_t b,
                      int32_t* ps, int32_t* parts) {
   if (partition_size == PA_PARTITION_AUTO) partition_size = auto_partition(base_units, max_len);
-  const int32_t whole = ((max_len > 0 ? max_len : 1) + b - 1) / b * b;
+  // One partition: whole 16-token tiles (8-token blocks then walk in pairs).
+  const int32_t unit = b < 16 ? 16 : b;
+  const int32_t whole = ((max_len > 0 ? max_len : 1) + unit - 1) / unit * unit;
   *ps = partition_size == 0 ? whole : partition_size;
   *parts = max_len > 0 ? (max_len + *ps - 1) / *ps : 1;
 }
@@ -784,14 +856,15 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   if (a.longest_first) lds = std::max(lds, (size_t)kRankLdsInts * sizeof(int));
   const hipStream_t s = (hipStream_t)stream;
   const int D = pool->head_dim;
+  const bool p8 = pool->block_size == 8 && ps % 16 == 0;
 
   switch (pool->dtype) {
     case PA_BF16:
-      return out_dtype == PA_F32 ? dispatch_d<TagBF16, float>(D, a, units, lds, s)
-                                 : dispatch_d<TagBF16, __bf16>(D, a, units, lds, s);
+      return out_dtype == PA_F32 ? dispatch_16<TagBF16, float>(p8, D, a, units, lds, s)
+                                 : dispatch_16<TagBF16, __bf16>(p8, D, a, units, lds, s);
     case PA_F16:
-      return out_dtype == PA_F32 ? dispatch_d<TagF16, float>(D, a, units, lds, s)
-                                 : dispatch_d<TagF16, _Float16>(D, a, units, lds, s);
+      return out_dtype == PA_F32 ? dispatch_16<TagF16, float>(p8, D, a, units, lds, s)
+                                 : dispatch_16<TagF16, _Float16>(p8, D, a, units, lds, s);
     case PA_FP8_E4M3:
       return out_dtype == PA_F32 ? dispatch_d<TagFP8, float>(D, a, units, lds, s)
                                  : dispatch_d<TagFP8, __bf16>(D, a, units, lds, s);

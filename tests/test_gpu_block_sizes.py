@@ -180,3 +180,34 @@ def test_gqa_batch256_full_size_sampled(b):
     announce(f"gqa-bf16-b256 b={b}: max row rel err {err:.3e}")
     assert np.isfinite(out).all()
     assert err <= 2e-3
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["three-calls", "fused"])
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_out_of_pool_entry_contributes_nothing(b, fused):
+    """A table entry outside the pool drops that block's tokens and nothing else.
+    At b = 8 blocks are walked in pairs: the bad entry is the first block of a
+    pair (sequence 0), the second (sequence 1), and the block just before the
+    current token's block, which is the second of its pair (sequence 2: the
+    token moves up a tile when its pair partner drops out)."""
+    from oracle import attention as OA
+    lengths = [9 * b + 3, 9 * b + 5, 7 * b + 4]
+    w = W.independent("b-bad", 92, "bf16", lengths, 8, 2, 128, _blocks_for(lengths, b), block_size=b)
+    batch = build_batch(w, drop_payload_cache=False)
+    bad = {0: 2, 1: 3, 2: (lengths[2] - 1) // b - 1}
+    assert ((lengths[2] - 1) // b) % 2 == 1
+    tab = batch.tables.clone()
+    for i, j in bad.items():
+        tab[i, j] = w.num_blocks + 3 + i
+    batch.tables = tab
+    out = DecodeStep(batch, partition_size=0, fused=fused)().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    run = OracleRun(w)
+    q = run.q64()
+    for i in range(w.num_seqs):
+        K, V = run.logical_kv(i)
+        keep = [t for t in range(K.shape[0]) if t // b != bad[i]]
+        ref = OA.decode_sequence(q[i], K[keep], V[keep], w.scale)
+        err = row_rel_err(out[i:i + 1], ref[None])
+        announce(f"b={b} fused={fused} seq {i} (bad block {bad[i]}): max row rel err {err:.3e}")
+        assert err <= 2e-3
