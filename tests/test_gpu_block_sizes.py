@@ -52,6 +52,10 @@ CASES = {
                                           128, 200 * 16 // b, block_size=b),
     "recycled-bf16": lambda b: W.independent("b-rec", 88, "bf16", [3 * b + 5, b, 7], 4, 1, 64,
                                              12, block_size=b, ghosts=[5 * b + 2, 2 * b]),
+    # 16-bit group shapes of the paired 8-token path: G = 16, 1 and 6
+    "gqa16-bf16-d128": lambda b: W.scaled("b-g16", 93, 5, 1, 400, 16, 1, 128, "bf16", block_size=b),
+    "mha-bf16-d64": lambda b: W.scaled("b-mb", 94, 5, 1, 400, 4, 4, 64, "bf16", block_size=b),
+    "gqa6-f16-d128": lambda b: W.scaled("b-g6", 95, 5, 1, 400, 12, 2, 128, "f16", block_size=b),
 }
 
 
@@ -147,7 +151,8 @@ def _poison_current_tokens(batch):
 @pytest.mark.parametrize("b", SIZES)
 @pytest.mark.parametrize("name,ps", [("gqa4-bf16-d128", 0), ("gqa8-f16-d64", 0),
                                      ("gqa3-f32-d128", 64), ("edges-bf16", 0),
-                                     ("cow-bf16", 0), ("recycled-bf16", 0)])
+                                     ("cow-bf16", 0), ("recycled-bf16", 0),
+                                     ("gqa16-bf16-d128", 0), ("gqa6-f16-d128", 512)])
 def test_fused_step_equals_three_calls_and_oracle(name, ps, b):
     w = CASES[name](b)
     outs, pools = [], []
