@@ -14,9 +14,12 @@
 // Work decomposition.  A workgroup of 4 wavefronts owns one work unit:
 // (KV head g, sequence i, partition p) where a partition is `ps`
 // consecutive positions (the whole sequence when ps covers it).  Wavefront w
-// takes the unit's blocks j = j0 + w, j0 + w + 4, ...  Per block it
-//   1. reads the physical id from the table (a register loaded once for up to
-//      64 blocks, broadcast with readlane),
+// takes the w-th contiguous quarter of the unit's blocks (on a pool where a
+// sequence holds consecutive blocks, four wavefronts reading neighbouring
+// blocks at the same moment ran 7 % slower than four reading far apart).
+// Per block it
+//   1. takes its address and stored count from registers built once for up
+//      to 64 blocks (one per lane) and broadcast with readlane,
 //   2. loads the K tile (4 KiB: 4 x 1 KiB fully contiguous dwordx4 loads per
 //      wavefront, for 16 x 128 16-bit elements) and the V tile (8 x 512 B
 //      contiguous dwordx2 loads), one block ahead of the computation,
@@ -461,8 +464,9 @@ void decode_kernel(DecodeArgs a) {
   const int nsub_seq = (L + rows - 1) / rows;
   const int j0 = part * (a.ps / rows);
   const int j1 = min(nsub_seq, j0 + a.ps / rows);
-  const int first = j0 + wave;
-  const int cnt = first < j1 ? (j1 - first + kWaves - 1) / kWaves : 0;
+  const int per = (j1 - j0 + kWaves - 1) / kWaves;  // tiles per wavefront: contiguous quarters
+  const int first = min(j1, j0 + wave * per);
+  const int cnt = max(0, min(j1, first + per) - first);
 
   const int h = lane & 15;
   QFrag<Tag, D> qf;
@@ -548,7 +552,7 @@ void decode_kernel(DecodeArgs a) {
   };
   auto open_chunk = [&]() {
     n = min(kWave, cnt - c0);
-    const int j = first + kWaves * (c0 + lane);
+    const int j = first + c0 + lane;
     if constexpr (P8) {
       // Blocks 2j and 2j+1.  Decode has no causal order, so valid blocks are
       // packed first and the tile's valid rows stay a prefix: block a out of
