@@ -68,20 +68,52 @@ def _workloads():
     }
 
 
+def _code_text(src: str) -> str:
+    """The source with C/C++ comments removed and whitespace runs collapsed:
+    what the compiler sees, so that editing a comment does not count as
+    changing the kernel."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the decode kernel's sources (comments and whitespace runs
+    removed), the key of the committed counter record."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_text(fh.read()).encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def _measured_traffic(fused: bool, partition: int):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record, only while the kernel sources are the ones it was taken on (and for
     the configuration it was taken in); otherwise None."""
-    import hashlib
     try:
         rec = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if rec.get("kernel_source_sha256") != h.hexdigest() or not fused or partition != 0:
+    if rec.get("kernel_source_sha256") != kernel_source_digest() or not fused or partition != 0:
         return None
     return rec.get("traffic_bytes_per_launch")
 

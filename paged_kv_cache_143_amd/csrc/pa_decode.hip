@@ -514,7 +514,8 @@ void decode_kernel(DecodeArgs a) {
   // outside the pool, negated for the block that holds the current token,
   // which is patched first).  A block is then a lane broadcast, not address
   // arithmetic.  Blocks past the wavefront's last one (the ring's prefetch)
-  // get count 0 and a size-0 resource: no memory access, static wait counts.
+  // get count 0 and a size-0 resource: no memory access, static wait counts
+  // (P8 tiles read block 0's tile of the head instead, see open_chunk).
   const uint64_t k_base = (uint64_t)a.k_pool;
   const uint64_t v_delta = (uint64_t)a.v_pool - k_base;
   const int sub_shift = a.sub >> 1;          // sub-tiles per block: 1 or 2
@@ -603,8 +604,9 @@ void decode_kernel(DecodeArgs a) {
   // unconditional so that every computation waits only for its own block (a
   // conditional load makes the wait counts path-dependent and the compiler
   // falls back to waiting for everything); past the last block the load is an
-  // empty-resource one.  The ring index is a compile-time constant in the
-  // unrolled body (registers are never indexed at run time).
+  // empty-resource one (P8: a cached re-read).  The ring index is a
+  // compile-time constant in the unrolled body (registers are never indexed at
+  // run time).
   for (; c0 < cnt; c0 += kWave) {
     if (c0 > 0) open_chunk();
     for (int i = 0; i < n; i += NBuf) {
