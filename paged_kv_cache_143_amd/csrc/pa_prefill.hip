@@ -333,11 +333,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       d_lo = (uint32_t)addr;
       d_hi = (uint32_t)(addr >> 32);
     };
+    // Lane offsets.  An 8-row sub-tile (8-token blocks) has no rows 8..15:
+    // those lanes read rows 0..7 again (in bounds; their scores and V are
+    // masked since no sub-tile stores more than `rows` tokens).
     uint32_t kro[D / 32];
 #pragma unroll
     for (int m = 0; m < D / 32; ++m)
-      kro[m] = (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16 + m * a.rows * 64);
-    const uint32_t vro = (uint32_t)((lane >> 4) * (D * 8) + (lane & 15) * 8);
+      kro[m] = (uint32_t)(((lane & 15) & (a.rows - 1)) * 64 + (lane >> 4) * 16 + m * a.rows * 64);
+    const uint32_t vro = (uint32_t)(((lane >> 4) & (a.rows / 4 - 1)) * (D * 8) + (lane & 15) * 8);
 
     // One fragment buffer, refilled in phases: the next pair's K as soon as
     // this pair's S^T products are issued, its V once the P.V products are.
