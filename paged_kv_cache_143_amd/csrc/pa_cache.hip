@@ -82,6 +82,81 @@ __global__ void write_kv_kernel(char* __restrict__ k_pool, char* __restrict__ v_
   }
 }
 
+// 16-bit pools, many tokens (prefill chunks): one wavefront per 4 input
+// tokens and KV head.  A token whose slot opens an aligned group of 4 slots,
+// with the next three input tokens on the next three slots, leads that group:
+// the wavefront writes the group's 4 K rows (per 32-dim chunk, 4 x 64 bytes
+// contiguous) and its V group (4 tokens x head_dim elements, contiguous) as
+// whole 128-byte lines, reading 4 bytes (V) or 16 bytes (K) of the inputs per
+// lane.  A token inside a group led from an earlier input position was
+// written by that group's wavefront; every other token is written on its own
+// by 16 lanes as in write_kv_kernel.  Writes cost per line touched while
+// other traffic streams, and a lone token's V is 2 bytes in each of
+// head_dim / 4 lines, so grouped tokens cost about a quarter as much.
+__device__ inline bool group_lead(const int32_t* slots, int32_t n, int t, int64_t num_slots) {
+  if (t < 0 || t + 3 >= n) return false;
+  const int32_t s = slots[t];
+  if (s < 0 || (s & 3) != 0 || (int64_t)s + 3 >= num_slots) return false;
+  return slots[t + 1] == s + 1 && slots[t + 2] == s + 2 && slots[t + 3] == s + 3;
+}
+
+__global__ __launch_bounds__(64) void write_kv_groups_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, int64_t new_stride, const int32_t* __restrict__ slots,
+    int32_t n, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_slots) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x % num_heads;
+  const int t0 = (blockIdx.x / num_heads) * 4;
+  const int R = block_size < 16 ? block_size : 16;
+  // The group led from t0 .. t0 + 3, if any (at most one: a leader's next
+  // three tokens sit on slots that are not multiples of 4).
+  int lead = -1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (lead < 0 && group_lead(slots, n, t0 + k, num_slots)) lead = t0 + k;
+  if (lead >= 0 && lane < head_dim / 2) {
+    const int32_t s = slots[lead];
+    const int32_t blk = s / block_size;
+    const int32_t o = s - blk * block_size;                    // multiple of 4
+    const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)block_size * head_dim * 2;
+    // K: lane -> (chunk m, row r, 16-byte quarter q) of the group's 4 rows.
+    const int m = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+    const int64_t ks = ((int64_t)(lead + r) * new_stride + (int64_t)h * head_dim + m * 32 + q * 8) * 2;
+    const int64_t kd = tile + (int64_t)(o / R) * R * head_dim * 2 + m * R * 64 +
+                       (int64_t)((o % R) + r) * 64 + q * 16;
+    *reinterpret_cast<u32x4*>(k_pool + kd) = *reinterpret_cast<const u32x4*>(k_new + ks);
+    // V: lane -> dims 2 lane, 2 lane + 1 of the 4 tokens: 16 contiguous bytes.
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = *reinterpret_cast<const uint32_t*>(
+          v_new + ((int64_t)(lead + j) * new_stride + (int64_t)h * head_dim + 2 * lane) * 2);
+    const u32x4 vv = {(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16),
+                      (w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+    *reinterpret_cast<u32x4*>(v_pool + tile + (int64_t)(o >> 2) * head_dim * 8 + lane * 16) = vv;
+  }
+  // Tokens of t0 .. t0 + 3 outside every group: 16 lanes each.
+  const int t = t0 + (lane >> 4);
+  const int c = lane & 15;
+  if (t >= n || c >= head_dim / 8) return;
+  const int32_t slot = slots[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  if (lead >= 0 && t >= lead && t < lead + 4) return;           // in this wavefront's group
+  if (group_lead(slots, n, t - (slot & 3), num_slots) && slots[t - (slot & 3)] == slot - (slot & 3))
+    return;                                                     // in an earlier group
+  const int32_t blk = slot / block_size;
+  const int32_t off = slot - blk * block_size;
+  const int64_t src = ((int64_t)t * new_stride + (int64_t)h * head_dim + (int64_t)c * 8) * 2;
+  const int64_t tile = ((int64_t)blk * num_heads + h) * (int64_t)block_size * head_dim;  // elements
+  *reinterpret_cast<u32x4*>(k_pool + tile * 2 + k16_offset(off, c * 8, block_size, head_dim)) =
+      *reinterpret_cast<const u32x4*>(k_new + src);
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + src);
+  char* vb = v_pool + (tile + ((int64_t)(off >> 2) * head_dim + (int64_t)c * 8) * 4 + (off & 3)) * 2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    *reinterpret_cast<uint16_t*>(vb + (int64_t)e * 8) = (uint16_t)(vv[e >> 1] >> ((e & 1) * 16));
+}
+
 // FP8 pools: bf16 inputs; a thread quantizes 16 consecutive dims of one
 // (token, head) with that head's scales into one 16-byte K store and 16
 // one-byte V stores, at the offsets of the FP8 tile layout.
@@ -308,7 +383,13 @@ pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, cons
         (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
         slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots,
         pool->k_scales, pool->v_scales);
-  else if (es == 2)
+  else if (es == 2 && n >= 4) {
+    const int64_t groups = ((int64_t)n + 3) / 4 * pool->num_kv_heads;
+    if (groups > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    write_kv_groups_kernel<<<(unsigned)groups, 64, 0, (hipStream_t)stream>>>(
+        (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
+        slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots);
+  } else if (es == 2)
     write_kv_kernel<2><<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
         (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
         slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots);

@@ -119,6 +119,50 @@ def test_write_kv_strided_rows_and_skips(dtype, D):
     assert_pool_equal(got_v, want_v)
 
 
+@pytest.mark.parametrize("dtype,D,b", [("bf16", 128, 16), ("f16", 64, 8), ("bf16", 128, 32),
+                                       ("f16", 128, 8), ("bf16", 64, 32)])
+def test_write_kv_runs_of_consecutive_slots(dtype, D, b):
+    """Many-token writes (prefill chunks): runs of consecutive slots starting at
+    every offset mod 4, crossing block boundaries, broken by skipped slots, next
+    to single scattered tokens -- the layouts a grouped write must get right --
+    land bit-exactly, every other slot keeping its poison."""
+    Hkv, nb = 2, 24
+    kv = PagedKV(nb, Hkv, D, dtype, poison=True, block_size=b)
+    rng = np.random.default_rng(11)
+    lens = [2 * b + 5, 3, 7, b + 6, 1, 4 * b, 9, 6]
+    gaps = [0, 2, 1, 3, 2, 2, 2, 3]
+    starts, cur = [], 0
+    for L, gap in zip(lens, gaps):
+        starts.append(cur + gap)
+        cur += gap + L
+    assert {s0 % 4 for s0 in starts} == {0, 1, 2, 3} and cur <= nb * b
+    slots = np.concatenate([np.arange(s0, s0 + L) for s0, L in zip(starts, lens)])
+    perm = rng.permutation(nb * b)
+    lone = [x for x in perm if x not in set(slots.tolist())][:11]
+    slots = np.concatenate([slots[:20], lone[:5], slots[20:], lone[5:]]).astype(np.int32)
+    slots[rng.choice(len(slots), 4, replace=False)] = -1
+    slots[9] = nb * b + 2
+    assert len(set(x for x in slots.tolist() if 0 <= x < nb * b)) == sum(1 for x in slots if 0 <= x < nb * b)
+    n = len(slots)
+    extra = 24
+    row = 2 * Hkv * D + extra
+    fused = W.normal((n, row), (98, 2, D), dtype)
+    k_new = fused.cuda()[:, :Hkv * D].view(n, Hkv, D)
+    v_new = fused.cuda()[:, Hkv * D:2 * Hkv * D].view(n, Hkv, D)
+    kv.write(k_new, v_new, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    pool = SlotPool(nb, b)
+    for t in range(n):
+        if 0 <= slots[t] < nb * b:
+            pool.write(int(slots[t]), t)
+    kf = fused[:, :Hkv * D].reshape(n, Hkv, D).to(torch.float64).numpy()
+    vf = fused[:, Hkv * D:2 * Hkv * D].reshape(n, Hkv, D).to(torch.float64).numpy()
+    want_k, want_v = pool.materialize(lambda t: (kf[t], vf[t]), Hkv, D)
+    got_k, got_v = pool_logical(kv, Hkv, D)
+    assert_pool_equal(got_k, want_k)
+    assert_pool_equal(got_v, want_v)
+
+
 def test_copy_blocks_direct_and_skips():
     w = WORKLOADS["gqa-bf16-d128"]()
     batch = build_batch(w, drop_payload_cache=False)
