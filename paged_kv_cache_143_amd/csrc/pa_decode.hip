@@ -125,7 +125,11 @@ __device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
 #pragma unroll
   for (int b = 0; b < kPer; ++b) hist[t * kPer + b] = 0;
   __syncthreads();
-  for (int i = t; i < S; i += kThreads) atomicAdd(&hist[rank_bin(a, i)], 1);
+  // Each thread's first sequence's bin, kept for the final pass: one round
+  // of length reads per workgroup when S <= kThreads (1 us of the launch).
+  const int my_bin = t < S ? rank_bin(a, t) : -1;
+  if (t < S) atomicAdd(&hist[my_bin], 1);
+  for (int i = t + kThreads; i < S; i += kThreads) atomicAdd(&hist[rank_bin(a, i)], 1);
   __syncthreads();
   // Exclusive prefix of the bin counts, kPer bins per thread.
   int c = 0;
@@ -160,7 +164,7 @@ __device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
   // The `within`-th sequence (by index) of that bin.
   for (int base = 0; base < S; base += kThreads) {
     const int i = base + t;
-    const bool hit = i < S && rank_bin(a, i) == bin;
+    const bool hit = i < S && (base == 0 ? my_bin : rank_bin(a, i)) == bin;
     const unsigned long long m = __ballot(hit);
     if (lane == 0) scratch[w] = __popcll(m);
     __syncthreads();
