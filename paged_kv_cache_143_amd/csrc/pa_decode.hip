@@ -3,7 +3,8 @@
 // What it computes: for sequence i, query head h (KV head g = h / G) and the
 // L_i tokens stored through block table i,
 //     out[i][h] = sum_t softmax_t(scale * q[i][h] . K_i[t][g]) V_i[t][g],
-// with K_i[t] read at offset t % 16 of physical block table_i[t / 16]
+// with K_i[t] read at offset t % b of physical block table_i[t / b] (b-token
+// blocks, b = 8, 16 or 32)
 // ("vLLM and PagedAttention: Virtual Memory for LLM Serving", paragraph 3:
 // the kernel reads through the block table and token order stays correct;
 // "Inside vLLM and TGI: Paging, Versioned Schedulers and Operations",
@@ -24,7 +25,7 @@
 //      wavefront, for 16 x 128 16-bit elements) and the V tile (8 x 512 B
 //      contiguous dwordx2 loads), one block ahead of the computation,
 //   3. S[t][h] = K[t] . q[h] on the matrix cores: v_mfma_f32_16x16x32 with the
-//      16 tokens of the block as rows and the G <= 16 query heads of the group
+//      16 tokens of the tile as rows and the G <= 16 query heads of the group
 //      as columns (rows of q beyond G are zero), accumulated over head_dim,
 //   4. online softmax on the 16 x G scores (wavefront max across the four
 //      16-lane rows), in the log2 domain,
@@ -75,7 +76,7 @@ struct DecodeArgs {
   int32_t num_seqs;
   int32_t max_blocks;  // table row width
   int32_t max_len;     // clip for lengths
-  int32_t ps;          // partition size in tokens (multiple of 16)
+  int32_t ps;          // partition size in tokens (a multiple of the block size)
   int32_t num_parts;   // P = ceil(max_len / ps)
   int32_t longest_first;  // 1: map workgroups to sequences in decreasing length
   float qk_scale;      // scale * log2(e)
