@@ -16,21 +16,26 @@
 // Work decomposition.  A column is one (chunk row, query head of group g)
 // pair; a 16-column group packs floor(16 / G) consecutive rows times the G
 // heads of the group.  A wavefront owns NQ column groups and walks the
-// sequence's 16-token sub-tiles from position 0 up to its last row's
-// position: S^T = K q^T on the matrix cores, a causal mask per column, online
-// softmax, O^T += V^T P^T with P split into high and low 16-bit halves.  Each
-// K/V fragment serves NQ groups; the four wavefronts of a workgroup take
-// consecutive row ranges of one (sequence, KV head) and re-read the same
-// tiles, which the L1 and L2 serve (cached loads, unlike decode's streaming
-// ones).  For 16-bit pools a step is two sub-tiles held in one register
-// buffer that is refilled in phases (the next K once this step's S^T products
-// are issued, the next V once its P.V products are), which keeps the kernel
-// under 256 registers: two wavefronts per SIMD.  Sub-tile addresses are built
-// 64 at a time, one per lane, and broadcast per step.  FP8 and fp32 pools take
-// one sub-tile per step with a second buffer one step ahead.  Each XCD runs
-// the row tiles of one (sequence, KV head) after another, last rows (the most
-// keys) first, so its resident workgroups share K/V in its L2.
+// sequence's keys from position 0 up to its last row's position: S^T = K q^T
+// on the matrix cores, a causal mask per column, online softmax, O^T += V^T
+// P^T with P split into high and low 16-bit halves.  Each K/V fragment serves
+// NQ groups; the four wavefronts of a workgroup take consecutive row ranges of
+// one (sequence, KV head).
+//
+// 16-bit pools (prefill_ring_kernel): the four wavefronts walk together in
+// steps of 32 keys.  Each step's K and V are copied once per workgroup from
+// the pool into a three-stage LDS ring by global-to-LDS loads issued two
+// steps ahead (the loading lanes gather the rows through the block table),
+// and every wavefront reads its fragments from LDS.  Table entries come in
+// windows of 64 blocks, one per lane, and reach the loading lanes by lane
+// permutation.  FP8 and fp32 pools (prefill_kernel): each wavefront walks on
+// its own, one sub-tile per step with a second buffer one step ahead, through
+// cached buffer loads.  Each XCD runs the row tiles of one (sequence, KV head)
+// after another, last rows (the most keys) first, so its resident workgroups
+// share K/V in its L2.
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "pa_tile.h"
 
@@ -61,57 +66,13 @@ template <> __device__ inline f32x2 unpack2<TagF16>(uint32_t w) {
   return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
 }
 
-typedef const __attribute__((address_space(1))) char* gchar;
-
+// K and V fragments of one step (two 16-row tiles a and b), read from LDS.
 template <class Tag, int D> struct FragPair {
-  u32x4 k[2][D / 32];     // K of sub-tiles a and b (the Frag<Tag> lane roles)
-  u32x4 v[D / 16];        // dim tile n: .xy = sub-tile a's 4 tokens, .zw = b's
-  // ka, kb: the two K sub-tiles (wave-uniform); kro[m]: this lane's byte
-  // offset of K dims 32m.. (rows-dependent).  Plain cached global loads.
-  __device__ inline void load_k(gchar ka, gchar kb, const uint32_t* kro) {
-#pragma unroll
-    for (int m = 0; m < D / 32; ++m) {
-      // The empty statement pins the 32-bit offset here, so the address stays
-      // "uniform base + zero-extended lane offset" (one load, no 64-bit adds)
-      // instead of a hoisted 64-bit per-lane value.
-      uint32_t o = kro[m];
-      asm volatile("" : "+v"(o));
-      k[0][m] = *(const __attribute__((address_space(1))) u32x4*)(ka + o);
-      k[1][m] = *(const __attribute__((address_space(1))) u32x4*)(kb + o);
-    }
-  }
-  // va, vb: the two V sub-tiles; vr: this lane's byte offset of V dim-tile 0
-  // (tile n adds 128 n).
-  __device__ inline void load_v(gchar va, gchar vb, uint32_t vr) {
-    asm volatile("" : "+v"(vr));
-#pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
-      const u32x2 x = *(const __attribute__((address_space(1))) u32x2*)(va + vr + n * 128);
-      const u32x2 y = *(const __attribute__((address_space(1))) u32x2*)(vb + vr + n * 128);
-      v[n] = u32x4{x[0], x[1], y[0], y[1]};
-    }
-  }
+  u32x4 k[2][D / 32];     // K of tiles a and b (the Frag<Tag> lane roles)
+  u32x4 v[D / 16];        // dim tile n: .xy = tile a's 4 tokens, .zw = b's
 };
 
-// Zero the V tokens at and past each sub-tile's stored count, in place (a
-// tail may hold NaN, and 0 * NaN would reach the accumulators).  The masks
-// depend on the stored counts only, so one pass serves every column group.
-template <class Tag, int D>
-__device__ inline void mask_v_tails(FragPair<Tag, D>& f, int nva, int nvb, int lane) {
-  const int t0 = 4 * (lane >> 4);
-  uint32_t keep[4];
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    keep[w] = (t0 + 2 * w < nva ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nva ? 0xffff0000u : 0u);
-    keep[2 + w] = (t0 + 2 * w < nvb ? 0x0000ffffu : 0u) | (t0 + 2 * w + 1 < nvb ? 0xffff0000u : 0u);
-  }
-#pragma unroll
-  for (int n = 0; n < D / 16; ++n)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.v[n][e] &= keep[e];
-}
-
-// S^T of the pair's two sub-tiles for one column group.
+// S^T of the step's two tiles for one column group.
 template <class Tag, int D>
 __device__ inline void qk_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& qf, f32x4& sa,
                                f32x4& sb) {
@@ -125,36 +86,45 @@ __device__ inline void qk_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& q
 }
 
 // Online softmax and O^T += V^T P^T for one column group, from its scores.
-// nva, nvb: stored tokens of the two sub-tiles (0 for none); lima, limb: per
-// lane, the column's causal limit in rows of each sub-tile (>= 16: all
-// visible).  V tails must already be masked (mask_v_tails).
+// valid: bit k set when key k of the step is stored (wave-uniform); lima: per
+// lane, the column's causal limit in rows of tile a (>= 32: the whole step is
+// visible; tile b's limit is lima - 16); c = scale * log2(e).  V rows of
+// invalid keys must already be zero.  On a step without masks the exponent
+// argument is one fma, and the lazy-rescale test uses the bound
+// |c| * max |s| >= max (c s), which may take the rescale branch when it is
+// not needed but never skips it when it is.
 template <class Tag, int D>
 __device__ inline void softmax_pv(const FragPair<Tag, D>& f, f32x4 sa, f32x4 sb, State<D>& st,
-                                  int nva, int nvb, float qk_scale, int lane, int lima,
-                                  int limb) {
+                                  uint32_t valid, float c, int lane, int lima) {
+  const float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+  const int limb = lima - kRows;
+  const bool masked = valid != 0xffffffffu || __builtin_amdgcn_ballot_w64(limb < kRows) != 0;
   float x[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    x[r] = sa[r] * qk_scale;
-    x[4 + r] = sb[r] * qk_scale;
-  }
-  if (nva < kRows || nvb < kRows ||
-      __builtin_amdgcn_ballot_w64(lima < kRows || limb < kRows) != 0) {
+  float ub;
+  if (masked) {
     const int t0 = 4 * (lane >> 4);
-    const int ea = min(nva, lima), eb = min(nvb, limb);
+    const uint32_t ma = valid >> t0, mb = valid >> (16 + t0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      // select, never multiply: tails may hold NaN
-      if (t0 + r >= ea) x[r] = -INFINITY;
-      if (t0 + r >= eb) x[4 + r] = -INFINITY;
+      // select, never multiply: invalid rows may hold NaN
+      x[r] = ((ma >> r) & 1u) && t0 + r < lima ? s[r] * c : -INFINITY;
+      x[4 + r] = ((mb >> r) & 1u) && t0 + r < limb ? s[4 + r] * c : -INFINITY;
     }
+    ub = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  } else {
+    const float am = fmaxf(fmaxf(fmaxf(fabsf(s[0]), fabsf(s[1])), fmaxf(fabsf(s[2]), fabsf(s[3]))),
+                           fmaxf(fmaxf(fabsf(s[4]), fabsf(s[5])), fmaxf(fabsf(s[6]), fabsf(s[7]))));
+    ub = am * fabsf(c);
   }
-  bool over = false;
+  if (__builtin_amdgcn_ballot_w64(ub > st.m + kRescaleLog2) != 0) {
+    float bm;
+    if (masked) {
+      bm = ub;
+    } else {
+      bm = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) over |= x[r] > st.m + kRescaleLog2;
-  if (__builtin_amdgcn_ballot_w64(over) != 0) {
-    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      for (int r = 0; r < 8; ++r) bm = fmaxf(bm, s[r] * c);
+    }
     bm = xor_max(bm);
     const float m_new = fmaxf(st.m, bm);
     const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.f : m_new));
@@ -165,8 +135,13 @@ __device__ inline void softmax_pv(const FragPair<Tag, D>& f, f32x4 sa, f32x4 sb,
   }
   const float base = st.m == -INFINITY ? 0.f : st.m;
   float p[8];
+  if (masked) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) p[r] = fast_exp2(x[r] - base);
+    for (int r = 0; r < 8; ++r) p[r] = fast_exp2(x[r] - base);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], c, -base));
+  }
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   u32x4 hi, lo;
 #pragma unroll
@@ -215,6 +190,293 @@ struct PrefillArgs {
   const float* k_scales;     // FP8 pools: per-KV-head scales, else null
   const float* v_scales;
 };
+
+// ---- 16-bit pools: steps staged in an LDS ring ------------------------------
+// A step is 32 consecutive key positions 32j .. 32j + 31: two 16-row tiles
+// (a: rows 0-15, b: rows 16-31), taken as four 8-row quarters, each inside
+// one block (8 divides the block size).  The four wavefronts of a workgroup
+// copy a step's K and V from the pool into one stage of a three-stage LDS ring
+// with global-to-LDS loads (1 KiB per instruction, no registers), two steps
+// ahead of the computation; every wavefront then reads its fragments from
+// LDS, so a tile leaves L2 once per workgroup rather than once per wavefront.
+//
+// Stage layout (16-bit elements; one 1-KiB chunk per load instruction):
+//   K chunk (h, m), m < D/32: [lane][16 B] = row lane % 16 of tile h, dims
+//     32m + 8 (lane / 16) .. +7 -- lane's A fragment, one ds_read_b128;
+//   V chunk n < D/16: [h][lane][8 B] = tokens 4 (lane / 16) .. +3 of tile h
+//     at dim 16n + lane % 16 -- both tiles' B halves, one ds_read2st64_b64.
+// The loading lanes gather these from the pool layout (include/pa.h): K
+// sub-tile [d/32][R][32] and V sub-tile [R/4][d][4], R = min(b, 16).
+template <int D> struct Ring {
+  static constexpr int kChunks = D / 32;                  // K chunks per tile
+  static constexpr int kKBytes = 2 * kChunks * 1024;
+  static constexpr int kStep = kKBytes + (D / 16) * 1024;
+  static constexpr int kStages = 3;
+  static constexpr int kPerWave = kStep / 1024 / kPWaves;  // load instructions per step
+  static_assert(kPerWave == kChunks, "waves 0-1 load K, waves 2-3 load V");
+};
+
+typedef const __attribute__((address_space(1))) char* gchar;
+typedef __attribute__((address_space(3))) char* lchar;
+typedef const __attribute__((address_space(4))) int32_t* cint;
+
+// LDS reads are written as instructions of their own: the compiler cannot
+// tell the ring's stages apart and would otherwise wait for every
+// outstanding global-to-LDS load before each read.  Their waits are explicit
+// (lgkm_wait), and `reg_after` orders a register's uses after such a wait.
+template <int OFF> __device__ inline u32x4 lds_read_b128(uint32_t addr) {
+  u32x4 x;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x) : "v"(addr), "n"(OFF));
+  return x;
+}
+template <int O64> __device__ inline u32x4 lds_read2st64_b64(uint32_t addr) {
+  u32x4 x;
+  asm volatile("ds_read2st64_b64 %0, %1 offset0:%2 offset1:%3"
+               : "=v"(x) : "v"(addr), "n"(O64), "n"(O64 + 1));
+  return x;
+}
+template <int N> __device__ inline void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N)); }
+template <int N> __device__ inline void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N)); }
+__device__ inline void reg_after(u32x4& x) { asm volatile("" : "+v"(x)); }
+
+// All K and V fragments of one stage (byte offset Base in the ring), with
+// the stage and chunk offsets in the instructions' offset fields.
+template <int Base, class Tag, int D, int... I>
+__device__ inline void read_k(FragPair<Tag, D>& f, uint32_t ka, std::integer_sequence<int, I...>) {
+  ((f.k[I / (D / 32)][I % (D / 32)] = lds_read_b128<Base + I * 1024>(ka)), ...);
+}
+template <int Base, class Tag, int D, int... I>
+__device__ inline void read_v(FragPair<Tag, D>& f, uint32_t va, std::integer_sequence<int, I...>) {
+  static_assert(Base % 512 == 0, "stage offsets are whole 512-byte units");
+  ((f.v[I] = lds_read2st64_b64<(Base + I * 1024) / 512>(va)), ...);
+}
+
+template <class Tag, int D, int NQ, class OutT>
+__global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) {
+  using RG = Ring<D>;
+  __shared__ __attribute__((aligned(1024))) char ring[RG::kStages * RG::kStep];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  // Workgroup order: as in prefill_kernel below.
+  const int xcd = blockIdx.x % kXcds;
+  const int k = blockIdx.x / kXcds;
+  const int pair = xcd + kXcds * (k / a.num_tiles);
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int seq = pair / a.num_kv_heads;
+  const int g = pair - seq * a.num_kv_heads;
+  const int tile = a.num_tiles - 1 - k % a.num_tiles;
+
+  const int qs = a.q_start[seq];
+  const int n = a.q_start[seq + 1] - qs;
+  int L = a.lens[seq];
+  L = L < 0 ? 0 : L;
+  L = L > a.max_len ? a.max_len : L;
+  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
+  if ((int64_t)L > cap) L = (int)cap;
+
+  // The whole workgroup leaves together or not at all (barriers below);
+  // a wavefront without rows still loads its share of every step.
+  const int wg_row0 = tile * kPWaves * a.wave_rows;
+  if (wg_row0 >= n) return;
+  const int wg_end = min(n, wg_row0 + kPWaves * a.wave_rows);
+  const int row0 = wg_row0 + wave * a.wave_rows;
+  const int row_end = min(n, row0 + a.wave_rows);
+  const int G = a.group;
+  const int head0 = g * G;
+
+  const int c = lane & 15;
+  const int cr = c / G;
+  const int chh = c - cr * G;
+  const bool col_ok = c < a.tpg * G;
+  QFrag<Tag, D> qf[NQ];
+  int pos[NQ];
+  bool has[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int t = row0 + q * a.tpg + cr;
+    const int p = L - n + t;
+    has[q] = col_ok && t < row_end && p >= 0;
+    pos[q] = has[q] ? p : 0;              // idle columns see key 0 only (their q is 0)
+    const int64_t qrow = has[q] ? ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) : 0;
+    qf[q].load(a.q + qrow * D * 2, has[q], lane);
+  }
+  State<D> st[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    st[q].m = -INFINITY;
+    st[q].l = 0.f;
+#pragma unroll
+    for (int d = 0; d < D / 16; ++d) st[q].acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Keys 0 .. p_wave for this wavefront's rows, 0 .. p_wg for the workgroup's.
+  const int p_wave = row0 < n ? L - n + row_end - 1 : -1;
+  const int p_wg = L - n + wg_end - 1;
+  const int nsteps = p_wg >= 0 ? p_wg / 32 + 1 : 0;
+
+  const int R = a.rows;
+  const int r_shift = R == 8 ? 3 : 4;
+  const int b_shift = a.block_size == 8 ? 3 : a.block_size == 16 ? 4 : 5;
+  const int64_t tile_bytes = (int64_t)a.block_size * D * 2;
+  const int sub_bytes = R * D * 2;
+  const uint32_t block_stride = (uint32_t)(a.num_kv_heads * tile_bytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lchar)ring;
+
+  // Each lane's part of a step's loads, fixed for the whole walk: wavefront
+  // h < 2 loads K of tile h, lane (t, piece) = (lane % 16, lane / 16);
+  // wavefronts 2-3 load V, lane (tile, token group, dim pair) = (lane / 32,
+  // (lane / 8) % 4, lane % 8).  The lane's rows lie in quarter qi (keys
+  // 8 qi .. 8 qi + 7 of the step), in block qblk counted from the step's
+  // first block (a step starts on a block boundary), at byte offset
+  // lane_off inside that block's tile of this KV head.
+  const int qi = wave < 2 ? 2 * wave + ((lane >> 3) & 1) : (lane >> 4) & 3;
+  const int in_blk = (8 * qi) & (a.block_size - 1);
+  const int qblk = (8 * qi) >> b_shift;
+  const int row_q = in_blk & (R - 1);
+  const uint32_t lane_off =
+      (uint32_t)((in_blk >> r_shift) * sub_bytes) +
+      (wave < 2 ? (uint32_t)((row_q + (lane & 7)) * 64 + (lane >> 4) * 16)
+                : (uint32_t)(((row_q >> 2) + ((lane >> 3) & 1)) * D * 8 + (lane & 7) * 16));
+  const uint64_t lane_base = (wave < 2 ? (uint64_t)a.k_pool : (uint64_t)a.v_pool) +
+                             (uint64_t)((int64_t)g * tile_bytes) + lane_off;
+
+  // Table window: lane i holds block B0 + i's physical id (0 when outside
+  // the pool or past the stored length, so every address stays in the
+  // pool); okw bit i says whether that block holds stored keys.
+  const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
+  const int blocks_per_step = 32 >> b_shift;
+  int B0 = 0;
+  int win = 0;
+  uint64_t okw = 0;
+  auto load_window = [&](int b0) {
+    B0 = b0;
+    const int B = b0 + lane;
+    const int phys = (int64_t)B * a.block_size < L ? trow[B] : -1;
+    const bool ok = phys >= 0 && phys < a.num_blocks;
+    win = ok ? phys : 0;
+    okw = __builtin_amdgcn_ballot_w64(ok);
+  };
+  load_window(0);
+
+  // Issue the loads of step j into stage `stg`; returns the step's valid-key
+  // bits (key k: position 32 j + k is below L and its block is in the pool).
+  auto issue = [&](int j, int stg) -> uint32_t {
+    const int Bs = (32 * j) >> b_shift;        // the step's first block
+    if (Bs + blocks_per_step > B0 + kWave) load_window(Bs);
+    const int phys = __builtin_amdgcn_ds_bpermute((Bs - B0 + qblk) * 4, win);
+    const uint64_t src = lane_base + (uint64_t)(uint32_t)phys * block_stride;
+    const uint32_t dst = lds0 + stg * RG::kStep;
+    if (wave < 2) {
+#pragma unroll
+      for (int m = 0; m < RG::kChunks; ++m)
+        __builtin_amdgcn_global_load_lds((gchar)(src + (uint32_t)(m * R * 64)),
+                                         (lchar)(uintptr_t)(dst + (wave * RG::kChunks + m) * 1024),
+                                         16, 0, 0);
+    } else {
+      const int n0 = (wave - 2) * RG::kChunks;
+#pragma unroll
+      for (int i = 0; i < RG::kChunks; ++i)
+        __builtin_amdgcn_global_load_lds((gchar)(src + (uint32_t)((n0 + i) * 128)),
+                                         (lchar)(uintptr_t)(dst + RG::kKBytes + (n0 + i) * 1024),
+                                         16, 0, 0);
+    }
+    const uint32_t okq = (uint32_t)(okw >> (Bs - B0));     // bit k: block Bs + k
+    const uint32_t all = (1u << blocks_per_step) - 1u;
+    if (32 * j + 32 <= L && (okq & all) == all) return 0xffffffffu;
+    uint32_t valid = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nv = (okq >> ((8 * i) >> b_shift)) & 1u ? min(8, L - 32 * j - 8 * i) : 0;
+      valid |= nv > 0 ? ((1u << nv) - 1u) << (8 * i) : 0u;
+    }
+    return valid;
+  };
+
+  // Step j from stage S: fragments from LDS, S^T, softmax, P.V.  V rows of
+  // invalid keys are already zero in the stage (zero_v_rows).
+  const uint32_t ka = lds0 + lane * 16, va = lds0 + lane * 8;
+  auto compute = [&](auto stage_c, int j, uint32_t valid) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int base = S * RG::kStep;
+    FragPair<Tag, D> f;
+    read_k<base>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
+    read_v<base + RG::kKBytes>(f, va, std::make_integer_sequence<int, D / 16>());
+    lgkm_wait<D / 16>();                // K arrived (LDS reads complete in order)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < RG::kChunks; ++m) reg_after(f.k[h][m]);
+    f32x4 sa[NQ], sb[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], sa[q], sb[q]);
+    lgkm_wait<0>();
+#pragma unroll
+    for (int d = 0; d < D / 16; ++d) reg_after(f.v[d]);
+    const int key0 = 32 * j;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      softmax_pv<Tag, D>(f, sa[q], sb[q], st[q], valid, a.qk_scale, lane, pos[q] - key0 + 1);
+  };
+
+  // On a step with invalid keys, each V-loading lane zeroes the elements of
+  // those keys in the pieces it loaded (a tail past L or a block outside the
+  // pool may hold NaN, and 0 * NaN would reach the accumulators).  Piece
+  // (lane, chunk n) holds tokens 4 tg .. 4 tg + 3 of tile h, two dims.
+  auto zero_v_rows = [&](int stg, uint32_t valid) {
+    const uint32_t bits = valid >> (16 * (lane >> 5) + 4 * ((lane >> 3) & 3));
+    const uint32_t k0 = (bits & 1u ? 0x0000ffffu : 0u) | (bits & 2u ? 0xffff0000u : 0u);
+    const uint32_t k1 = (bits & 4u ? 0x0000ffffu : 0u) | (bits & 8u ? 0xffff0000u : 0u);
+    const int n0 = (wave - 2) * RG::kChunks;
+#pragma unroll
+    for (int i = 0; i < RG::kChunks; ++i) {
+      u32x4* piece = reinterpret_cast<u32x4*>(ring + stg * RG::kStep + RG::kKBytes +
+                                              (n0 + i) * 1024 + lane * 16);
+      const u32x4 x = *piece;
+      *piece = u32x4{x[0] & k0, x[1] & k1, x[2] & k0, x[3] & k1};
+    }
+  };
+
+  // Three-stage ring, two steps in flight.  Before step j: this wavefront's
+  // loads of step j are done (those of j + 1 may still run), then a barrier:
+  // every wavefront's loads of step j are in LDS and every wavefront is done
+  // reading step j - 1, whose stage the loads of step j + 2 then refill.
+  uint32_t valid[RG::kStages] = {0u, 0u, 0u};
+  if (nsteps > 0) valid[0] = issue(0, 0);
+  if (nsteps > 1) valid[1] = issue(1, 1);
+  auto step = [&](auto stage_c, int j) {
+    constexpr int S = decltype(stage_c)::value;
+    if (j + 1 < nsteps) vm_wait<RG::kPerWave>(); else vm_wait<0>();
+    if (wave >= 2 && valid[S] != 0xffffffffu) {   // this wavefront's V loads of step j are done
+      zero_v_rows(S, valid[S]);
+      lgkm_wait<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (j + 2 < nsteps) valid[(S + 2) % 3] = issue(j + 2, (S + 2) % 3);
+    if (32 * j <= p_wave) compute(stage_c, j, valid[S]);
+  };
+  for (int j = 0; j < nsteps; j += 3) {
+    step(std::integral_constant<int, 0>(), j);
+    if (j + 1 >= nsteps) break;
+    step(std::integral_constant<int, 1>(), j + 1);
+    if (j + 2 >= nsteps) break;
+    step(std::integral_constant<int, 2>(), j + 2);
+  }
+
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const float l_tot = xor_sum(st[q].l);
+    const int t = row0 + q * a.tpg + cr;
+    if (!(col_ok && t < row_end)) continue;
+    const float inv = (has[q] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    OutT* o = reinterpret_cast<OutT*>(a.out) +
+              ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) * D;
+#pragma unroll
+    for (int d = 0; d < D / 16; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store_out<OutT>(o + out_dim<Tag, D>(d, r, lane), st[q].acc[d][r] * inv);
+  }
+}
 
 template <class Tag, int D, int NQ, class OutT>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
@@ -312,112 +574,33 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     tb = lane < nc ? trow[(c0 + lane) / a.sub] : 0;
   };
 
-  if constexpr (Is16<Tag>::value && !IsFP8<Tag>::value) {
-    // Two sub-tiles per step, two steps in registers (one ahead).  Sub-tile
-    // descriptors are built 64 at a time, one per lane (K address and stored
-    // count), and read with lane broadcasts; a pair never straddles two sets.
-    // Sub-tiles past the walk or behind a table entry outside the pool get
-    // count 0 and the address of block 0's tile (in bounds: a pool holds at
-    // least one block), so every load is valid and the masks drop them.
-    const uint64_t k_base = (uint64_t)a.k_pool;
-    const uint64_t v_delta = (uint64_t)a.v_pool - k_base;
-    uint32_t d_lo = 0, d_hi = 0;
-    int d_nv = 0, dbase = -kWave;
-    auto open_set = [&](int first) {
-      const int j = first + lane;
-      const int phys = j < cnt ? trow[j / a.sub] : -1;
-      const bool ok = phys >= 0 && phys < a.num_blocks;
-      d_nv = ok ? min(a.rows, L - j * a.rows) : 0;
-      const uint64_t addr = k_base + (uint64_t)(ok ? phys : 0) * (uint64_t)block_stride +
-                            (uint64_t)head_tile + (uint64_t)(j % a.sub) * (uint64_t)sub_bytes;
-      d_lo = (uint32_t)addr;
-      d_hi = (uint32_t)(addr >> 32);
-    };
-    // Lane offsets.  An 8-row sub-tile (8-token blocks) has no rows 8..15:
-    // those lanes read rows 0..7 again (in bounds; their scores and V are
-    // masked since no sub-tile stores more than `rows` tokens).
-    uint32_t kro[D / 32];
+  Frag<Tag, D> fa, fb;
+  int nva = 0, nvb = 0;
+  auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
+    int64_t off;
+    int bytes;
+    locate(i, off, bytes, nv);
+    f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
+                                   tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
+  };
+  using CT = typename ComputeTag<Tag>::type;
+  auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
+    if (nv <= 0) return;
+    const int key0 = (c0 + i) * a.rows;
+    const Frag<CT, D> w = compute_regs(f);
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m)
-      kro[m] = (uint32_t)(((lane & 15) & (a.rows - 1)) * 64 + (lane >> 4) * 16 + m * a.rows * 64);
-    const uint32_t vro = (uint32_t)(((lane >> 4) & (a.rows / 4 - 1)) * (D * 8) + (lane & 15) * 8);
-
-    // One fragment buffer, refilled in phases: the next pair's K as soon as
-    // this pair's S^T products are issued, its V once the P.V products are.
-    FragPair<Tag, D> f;
-    int nv[2] = {0, 0};
-    uint64_t ka = 0, kb = 0;
-    auto locate_pair = [&](int P, int* n2) {
-      const int s0 = 2 * P;
-      if (s0 - dbase >= kWave) {
-        dbase += kWave;
-        open_set(dbase);
-      }
-      const int i = s0 - dbase;
-      ka = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(d_hi, i) << 32) |
-           (uint32_t)__builtin_amdgcn_readlane(d_lo, i);
-      kb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(d_hi, i + 1) << 32) |
-           (uint32_t)__builtin_amdgcn_readlane(d_lo, i + 1);
-      n2[0] = __builtin_amdgcn_readlane(d_nv, i);
-      n2[1] = __builtin_amdgcn_readlane(d_nv, i + 1);
-    };
-    const int np = (cnt + 1) / 2;
-    if (np > 0) {
-      locate_pair(0, nv);
-      f.load_k((gchar)ka, (gchar)kb, kro);
-      f.load_v((gchar)(ka + v_delta), (gchar)(kb + v_delta), vro);
-    }
-    for (int P = 0; P < np; ++P) {
-      const bool more = P + 1 < np;
-      int nn[2] = {0, 0};
-      f32x4 sa[NQ], sb[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], sa[q], sb[q]);
-      if (more) {
-        locate_pair(P + 1, nn);
-        f.load_k((gchar)ka, (gchar)kb, kro);
-      }
-      if (nv[0] > 0 || nv[1] > 0) {
-        if (nv[0] < kRows || nv[1] < kRows) mask_v_tails(f, nv[0], nv[1], lane);
-        const int key0 = 2 * P * a.rows;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          softmax_pv<Tag, D>(f, sa[q], sb[q], st[q], nv[0], nv[1], qk_scale, lane,
-                             pos[q] - key0 + 1, pos[q] - key0 - a.rows + 1);
-      }
-      if (more) f.load_v((gchar)(ka + v_delta), (gchar)(kb + v_delta), vro);
-      nv[0] = nn[0];
-      nv[1] = nn[1];
-    }
-  } else {
-    Frag<Tag, D> fa, fb;
-    int nva = 0, nvb = 0;
-    auto load_into = [&](Frag<Tag, D>& f, int i, int& nv) {
-      int64_t off;
-      int bytes;
-      locate(i, off, bytes, nv);
-      f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
-                                     tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
-    };
-    using CT = typename ComputeTag<Tag>::type;
-    auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
-      if (nv <= 0) return;
-      const int key0 = (c0 + i) * a.rows;
-      const Frag<CT, D> w = compute_regs(f);
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        attend_block<CT, D>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
-    };
-    for (; c0 < cnt; c0 += kWave) {
-      open_table();
-      load_into(fa, 0, nva);
-      for (int i = 0; i < nc; i += 2) {
-        load_into(fb, i + 1, nvb);
-        attend(fa, nva, i);
-        if (i + 1 >= nc) break;
-        load_into(fa, i + 2, nva);
-        attend(fb, nvb, i + 1);
-      }
+    for (int q = 0; q < NQ; ++q)
+      attend_block<CT, D>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
+  };
+  for (; c0 < cnt; c0 += kWave) {
+    open_table();
+    load_into(fa, 0, nva);
+    for (int i = 0; i < nc; i += 2) {
+      load_into(fb, i + 1, nvb);
+      attend(fa, nva, i);
+      if (i + 1 >= nc) break;
+      load_into(fa, i + 2, nva);
+      attend(fb, nvb, i + 1);
     }
   }
 
@@ -439,7 +622,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 
 template <class Tag, int D, class OutT>
 static pa_status launch_prefill(const PrefillArgs& a, int64_t units, hipStream_t s) {
-  prefill_kernel<Tag, D, kNQ, OutT><<<(unsigned)units, kPThreads, 0, s>>>(a);
+  if constexpr (Is16<Tag>::value && !IsFP8<Tag>::value)
+    prefill_ring_kernel<Tag, D, kNQ, OutT><<<(unsigned)units, kPThreads, 0, s>>>(a);
+  else
+    prefill_kernel<Tag, D, kNQ, OutT><<<(unsigned)units, kPThreads, 0, s>>>(a);
   return launch_status();
 }
 

@@ -1,26 +1,123 @@
-"""Every address of the two global-load paths stays inside its tile.
+"""Every address of the plain-load paths stays inside its tile or buffer.
 
 Buffer-resource loads are bounds-checked by the hardware (a lane past the
-resource reads zero); the 16-bit prefill fragments and the paired 8-token
-decode tiles use plain global loads from a uniform tile base plus a lane
-offset, so their offsets must stay within the tile on their own.  This test
-enumerates those lane offsets, written as in pa_prefill.hip (FragPair loads,
-kro/vro) and pa_decode.hip (load_pair8), for every supported sub-tile height
-and head dim, and checks them against the tile sizes of the pool layout in
-include/pa.h: a 16-bit sub-tile of R rows holds R * head_dim * 2 bytes of K
-and the same of V.  Runs on the CPU.
+resource reads zero).  Two paths use plain addresses and must stay in bounds
+on their own:
+
+* the 16-bit prefill ring (pa_prefill.hip): each step's K and V are copied
+  from the pool into an LDS stage by global-to-LDS loads, one 16-byte piece
+  per lane at a per-lane offset inside one block's tile of the KV head, and
+  read back by fragment loads at fixed LDS offsets;
+* the paired 8-token decode tiles (pa_decode.hip, load_pair8).
+
+This test re-derives those lane offsets, written as in the kernels, for every
+supported block size and head dim, and checks them against the tile sizes of
+the pool layout in include/pa.h (a 16-bit tile of b tokens holds b * head_dim
+* 2 bytes of K and the same of V) and against the LDS ring.  It also checks
+that a step's loads copy every byte of its 32 keys exactly once and that the
+LDS fragment reads see each key's data where the matrix-core layout expects
+it.  Runs on the CPU.
 """
 import pytest
 
+WAVES = 4
 
-def prefill_offsets(rows, D):
-    k, v = [], []
-    for lane in range(64):
-        for m in range(D // 32):
-            k.append(((lane & 15) & (rows - 1)) * 64 + (lane >> 4) * 16 + m * rows * 64)
-        for n in range(D // 16):
-            v.append(((lane >> 4) & (rows // 4 - 1)) * (D * 8) + (lane & 15) * 8 + n * 128)
-    return k, v
+
+def ring_dma(b, D):
+    """Per (wave, lane, instruction): (quarter qi, byte offset in the block's
+    tile, LDS byte offset in the stage) of the 16-byte piece it loads."""
+    R = min(b, 16)
+    r_shift = 3 if R == 8 else 4
+    sub_bytes = R * D * 2
+    chunks = D // 32
+    kbytes = 2 * chunks * 1024
+    out = []
+    for wave in range(WAVES):
+        for lane in range(64):
+            qi = 2 * wave + ((lane >> 3) & 1) if wave < 2 else (lane >> 4) & 3
+            in_blk = (8 * qi) & (b - 1)
+            row_q = in_blk & (R - 1)
+            if wave < 2:
+                off = (in_blk >> r_shift) * sub_bytes + (row_q + (lane & 7)) * 64 + (lane >> 4) * 16
+                for m in range(chunks):
+                    out.append((wave, lane, qi, off + m * R * 64, (wave * chunks + m) * 1024 + lane * 16))
+            else:
+                off = ((in_blk >> r_shift) * sub_bytes
+                       + ((row_q >> 2) + ((lane >> 3) & 1)) * D * 8 + (lane & 7) * 16)
+                n0 = (wave - 2) * chunks
+                for i in range(chunks):
+                    out.append((wave, lane, qi, off + (n0 + i) * 128, kbytes + (n0 + i) * 1024 + lane * 16))
+    return out
+
+
+def k_elem(b, D, t, d):
+    """Byte offset of K element (token t of the block, dim d) in a 16-bit tile."""
+    R = min(b, 16)
+    s, tl = divmod(t, R)
+    return (s * R * D + (d >> 5) * (R * 32) + tl * 32 + (d & 31)) * 2
+
+
+def v_elem(b, D, t, d):
+    R = min(b, 16)
+    s, tl = divmod(t, R)
+    return (s * R * D + (tl >> 2) * D * 4 + d * 4 + (tl & 3)) * 2
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_ring_loads_in_bounds(b, D):
+    tile = b * D * 2
+    step = 2 * (D // 32) * 1024 + (D // 16) * 1024
+    for wave, lane, qi, off, lds in ring_dma(b, D):
+        assert 0 <= off and off + 16 <= tile, (wave, lane, off)
+        assert 0 <= lds and lds + 16 <= step
+    # the instructions per wavefront are what the kernel's wait counts assume
+    per_wave = {}
+    for wave, lane, *_ in ring_dma(b, D):
+        per_wave[wave] = per_wave.get(wave, 0) + 1
+    assert all(n == 64 * (D // 32) for n in per_wave.values())
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_ring_copies_each_key_once(b, D):
+    """Build the step's 32 keys from (quarter, offset) pieces and check that
+    the LDS stage holds K row t / V token t of the step exactly where the
+    fragment reads look for them."""
+    # element id = (kind, key in step, dim); the pool block of a key is fixed
+    # by its quarter (8 keys), its position inside the block by the offset.
+    src = {}
+    for qi in range(4):
+        for kk in range(8):
+            key = 8 * qi + kk
+            t = ((8 * qi) & (b - 1)) + kk             # token inside its block
+            for d in range(D):
+                src[(qi, "K", k_elem(b, D, t, d))] = ("K", key, d)
+                src[(qi, "V", v_elem(b, D, t, d))] = ("V", key, d)
+    stage = {}
+    for wave, lane, qi, off, lds in ring_dma(b, D):
+        kind = "K" if wave < 2 else "V"
+        for e in range(8):                            # 8 two-byte elements per piece
+            item = src[(qi, kind, off + 2 * e)]
+            assert (lds + 2 * e) not in stage
+            stage[lds + 2 * e] = item
+    assert len(stage) == 2 * 32 * D                   # K and V of 32 keys, each once
+    chunks = D // 32
+    kbytes = 2 * chunks * 1024
+    # K fragment: chunk (h, m), lane (t, g) reads 8 dims 32m + 8g.. of row 16h + t
+    for h in range(2):
+        for m in range(chunks):
+            for lane in range(64):
+                t, g = lane & 15, lane >> 4
+                for e in range(8):
+                    assert stage[(h * chunks + m) * 1024 + lane * 16 + 2 * e] == ("K", 16 * h + t, 32 * m + 8 * g + e)
+    # V fragment: chunk n, tile h, lane (d, tg) reads tokens 4tg..4tg+3 of dim 16n + d
+    for n in range(D // 16):
+        for h in range(2):
+            for lane in range(64):
+                d, tg = lane & 15, lane >> 4
+                for e in range(4):
+                    assert stage[kbytes + n * 1024 + h * 512 + lane * 8 + 2 * e] == ("V", 16 * h + 4 * tg + e, 16 * n + d)
 
 
 def decode_pair8_offsets(D):
@@ -34,18 +131,6 @@ def decode_pair8_offsets(D):
         for n in range(D // 16):
             v.append((vb, ((lane >> 4) & 1) * (D * 8) + (lane & 15) * 8 + n * 128))
     return k, v
-
-
-@pytest.mark.parametrize("rows", [8, 16])
-@pytest.mark.parametrize("D", [64, 128])
-def test_prefill_fragment_loads_in_bounds(rows, D):
-    sub_bytes = rows * D * 2
-    k, v = prefill_offsets(rows, D)
-    assert min(k) >= 0 and max(k) + 16 <= sub_bytes     # 16-byte K pieces
-    assert min(v) >= 0 and max(v) + 8 <= sub_bytes      # 8-byte V pieces
-    # every byte of the sub-tile is read (nothing of the tile is skipped)
-    assert len({o + i for o in k for i in range(16)}) == sub_bytes
-    assert len({o + i for o in v for i in range(8)}) == sub_bytes
 
 
 @pytest.mark.parametrize("D", [64, 128])
