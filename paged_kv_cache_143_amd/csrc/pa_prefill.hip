@@ -24,9 +24,10 @@
 //
 // 16-bit pools (prefill_ring_kernel): the four wavefronts walk together in
 // steps of 32 keys.  Each step's K and V are copied once per workgroup from
-// the pool into a three-stage LDS ring by global-to-LDS loads issued two
+// the pool into a four-stage LDS ring by global-to-LDS loads issued three
 // steps ahead (the loading lanes gather the rows through the block table),
-// and every wavefront reads its fragments from LDS.  Table entries come in
+// and every wavefront reads its fragments from LDS, the next step's K while
+// the current step's softmax runs.  Table entries come in
 // windows of 64 blocks, one per lane, and reach the loading lanes by lane
 // permutation.  FP8 and fp32 pools (prefill_kernel): each wavefront walks on
 // its own, one sub-tile per step with a second buffer one step ahead, through
@@ -89,18 +90,20 @@ __device__ inline void qk_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& q
 // valid: bit k set when key k of the step is stored (wave-uniform); lima: per
 // lane, the column's causal limit in rows of tile a (>= 32: the whole step is
 // visible; tile b's limit is lima - 16); c = scale * log2(e).  V rows of
-// invalid keys must already be zero.  On a step without masks the exponent
-// argument is one fma, and the lazy-rescale test uses the bound
-// |c| * max |s| >= max (c s), which may take the rescale branch when it is
-// not needed but never skips it when it is.
+// invalid keys must already be zero.  The exponentials are taken against the
+// current base first and checked afterwards: only when one exceeds 2^8 (or
+// overflows), or the column has no base yet, does the wavefront move the
+// base to the running maximum, rescale l and acc, and take them again -- the
+// same softmax for any base, and no maximum of the scores on the common
+// path.  p >= 0, so its largest value is an integer maximum of the bit
+// patterns.
 template <class Tag, int D>
 __device__ inline void softmax_pv(const FragPair<Tag, D>& f, f32x4 sa, f32x4 sb, State<D>& st,
                                   uint32_t valid, float c, int lane, int lima) {
   const float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
   const int limb = lima - kRows;
   const bool masked = valid != 0xffffffffu || __builtin_amdgcn_ballot_w64(limb < kRows) != 0;
-  float x[8];
-  float ub;
+  float x[8];                 // exponent arguments before the base: c s, or -inf when masked
   if (masked) {
     const int t0 = 4 * (lane >> 4);
     const uint32_t ma = valid >> t0, mb = valid >> (16 + t0);
@@ -110,18 +113,29 @@ __device__ inline void softmax_pv(const FragPair<Tag, D>& f, f32x4 sa, f32x4 sb,
       x[r] = ((ma >> r) & 1u) && t0 + r < lima ? s[r] * c : -INFINITY;
       x[4 + r] = ((mb >> r) & 1u) && t0 + r < limb ? s[4 + r] * c : -INFINITY;
     }
-    ub = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  } else {
-    const float am = fmaxf(fmaxf(fmaxf(fabsf(s[0]), fabsf(s[1])), fmaxf(fabsf(s[2]), fabsf(s[3]))),
-                           fmaxf(fmaxf(fabsf(s[4]), fabsf(s[5])), fmaxf(fabsf(s[6]), fabsf(s[7]))));
-    ub = am * fabsf(c);
   }
-  if (__builtin_amdgcn_ballot_w64(ub > st.m + kRescaleLog2) != 0) {
-    float bm;
+  float p[8];
+  auto exps = [&]() {
+    const float base = st.m == -INFINITY ? 0.f : st.m;
     if (masked) {
-      bm = ub;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) p[r] = fast_exp2(x[r] - base);
     } else {
-      bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], c, -base));
+    }
+  };
+  exps();
+  const uint32_t pm = max(max(max(__float_as_uint(p[0]), __float_as_uint(p[1])), max(__float_as_uint(p[2]), __float_as_uint(p[3]))),
+           max(max(__float_as_uint(p[4]), __float_as_uint(p[5])), max(__float_as_uint(p[6]), __float_as_uint(p[7]))));
+  // Some p > 2^8 (= 256.0f), or a column still without a base (m = -inf:
+  // the exponentials above used base 0 only provisionally).
+  if (__builtin_amdgcn_ballot_w64(pm > 0x43800000u || st.m == -INFINITY) != 0) {
+    float bm = -INFINITY;
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) bm = fmaxf(bm, x[r]);
+    } else {
 #pragma unroll
       for (int r = 0; r < 8; ++r) bm = fmaxf(bm, s[r] * c);
     }
@@ -132,15 +146,7 @@ __device__ inline void softmax_pv(const FragPair<Tag, D>& f, f32x4 sa, f32x4 sb,
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) st.acc[n] *= alpha;
     st.m = m_new;
-  }
-  const float base = st.m == -INFINITY ? 0.f : st.m;
-  float p[8];
-  if (masked) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) p[r] = fast_exp2(x[r] - base);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], c, -base));
+    exps();
   }
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   u32x4 hi, lo;
@@ -195,8 +201,8 @@ struct PrefillArgs {
 // A step is 32 consecutive key positions 32j .. 32j + 31: two 16-row tiles
 // (a: rows 0-15, b: rows 16-31), taken as four 8-row quarters, each inside
 // one block (8 divides the block size).  The four wavefronts of a workgroup
-// copy a step's K and V from the pool into one stage of a three-stage LDS ring
-// with global-to-LDS loads (1 KiB per instruction, no registers), two steps
+// copy a step's K and V from the pool into one stage of a four-stage LDS ring
+// with global-to-LDS loads (1 KiB per instruction, no registers), three steps
 // ahead of the computation; every wavefront then reads its fragments from
 // LDS, so a tile leaves L2 once per workgroup rather than once per wavefront.
 //
@@ -211,7 +217,7 @@ template <int D> struct Ring {
   static constexpr int kChunks = D / 32;                  // K chunks per tile
   static constexpr int kKBytes = 2 * kChunks * 1024;
   static constexpr int kStep = kKBytes + (D / 16) * 1024;
-  static constexpr int kStages = 3;
+  static constexpr int kStages = 4;
   static constexpr int kPerWave = kStep / 1024 / kPWaves;  // load instructions per step
   static_assert(kPerWave == kChunks, "waves 0-1 load K, waves 2-3 load V");
 };
@@ -310,8 +316,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     for (int d = 0; d < D / 16; ++d) st[q].acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Keys 0 .. p_wave for this wavefront's rows, 0 .. p_wg for the workgroup's.
-  const int p_wave = row0 < n ? L - n + row_end - 1 : -1;
+  // Keys 0 .. p_wg for the workgroup's rows; every wavefront walks them all
+  // (keys past a wavefront's last row are masked by the causal limits).
   const int p_wg = L - n + wg_end - 1;
   const int nsteps = p_wg >= 0 ? p_wg / 32 + 1 : 0;
 
@@ -359,64 +365,51 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   };
   load_window(0);
 
-  // Issue the loads of step j into stage `stg`; returns the step's valid-key
-  // bits (key k: position 32 j + k is below L and its block is in the pool).
-  auto issue = [&](int j, int stg) -> uint32_t {
+  // Loads of step j, in two parts: `prepare` (table window, this lane's
+  // source address, the step's valid-key bits: key k valid when position
+  // 32 j + k is below L and its block is in the pool) runs before the
+  // barrier; `dma` copies into a stage, after it.
+  struct Prep {
+    uint64_t src;
+    uint32_t valid;
+  };
+  auto prepare = [&](int j) -> Prep {
     const int Bs = (32 * j) >> b_shift;        // the step's first block
     if (Bs + blocks_per_step > B0 + kWave) load_window(Bs);
     const int phys = __builtin_amdgcn_ds_bpermute((Bs - B0 + qblk) * 4, win);
-    const uint64_t src = lane_base + (uint64_t)(uint32_t)phys * block_stride;
+    Prep pr;
+    pr.src = lane_base + (uint64_t)(uint32_t)phys * block_stride;
+    const uint32_t okq = (uint32_t)(okw >> (Bs - B0));     // bit k: block Bs + k
+    const uint32_t all = (1u << blocks_per_step) - 1u;
+    if (32 * j + 32 <= L && (okq & all) == all) {
+      pr.valid = 0xffffffffu;
+    } else {
+      uint32_t valid = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nv = (okq >> ((8 * i) >> b_shift)) & 1u ? min(8, L - 32 * j - 8 * i) : 0;
+        valid |= nv > 0 ? ((1u << nv) - 1u) << (8 * i) : 0u;
+      }
+      pr.valid = valid;
+    }
+    return pr;
+  };
+  auto dma = [&](const Prep& pr, int stg) {
     const uint32_t dst = lds0 + stg * RG::kStep;
     if (wave < 2) {
 #pragma unroll
       for (int m = 0; m < RG::kChunks; ++m)
-        __builtin_amdgcn_global_load_lds((gchar)(src + (uint32_t)(m * R * 64)),
+        __builtin_amdgcn_global_load_lds((gchar)(pr.src + (uint32_t)(m * R * 64)),
                                          (lchar)(uintptr_t)(dst + (wave * RG::kChunks + m) * 1024),
                                          16, 0, 0);
     } else {
       const int n0 = (wave - 2) * RG::kChunks;
 #pragma unroll
       for (int i = 0; i < RG::kChunks; ++i)
-        __builtin_amdgcn_global_load_lds((gchar)(src + (uint32_t)((n0 + i) * 128)),
+        __builtin_amdgcn_global_load_lds((gchar)(pr.src + (uint32_t)((n0 + i) * 128)),
                                          (lchar)(uintptr_t)(dst + RG::kKBytes + (n0 + i) * 1024),
                                          16, 0, 0);
     }
-    const uint32_t okq = (uint32_t)(okw >> (Bs - B0));     // bit k: block Bs + k
-    const uint32_t all = (1u << blocks_per_step) - 1u;
-    if (32 * j + 32 <= L && (okq & all) == all) return 0xffffffffu;
-    uint32_t valid = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int nv = (okq >> ((8 * i) >> b_shift)) & 1u ? min(8, L - 32 * j - 8 * i) : 0;
-      valid |= nv > 0 ? ((1u << nv) - 1u) << (8 * i) : 0u;
-    }
-    return valid;
-  };
-
-  // Step j from stage S: fragments from LDS, S^T, softmax, P.V.  V rows of
-  // invalid keys are already zero in the stage (zero_v_rows).
-  const uint32_t ka = lds0 + lane * 16, va = lds0 + lane * 8;
-  auto compute = [&](auto stage_c, int j, uint32_t valid) {
-    constexpr int S = decltype(stage_c)::value;
-    constexpr int base = S * RG::kStep;
-    FragPair<Tag, D> f;
-    read_k<base>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
-    read_v<base + RG::kKBytes>(f, va, std::make_integer_sequence<int, D / 16>());
-    lgkm_wait<D / 16>();                // K arrived (LDS reads complete in order)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int m = 0; m < RG::kChunks; ++m) reg_after(f.k[h][m]);
-    f32x4 sa[NQ], sb[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], sa[q], sb[q]);
-    lgkm_wait<0>();
-#pragma unroll
-    for (int d = 0; d < D / 16; ++d) reg_after(f.v[d]);
-    const int key0 = 32 * j;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      softmax_pv<Tag, D>(f, sa[q], sb[q], st[q], valid, a.qk_scale, lane, pos[q] - key0 + 1);
   };
 
   // On a step with invalid keys, each V-loading lane zeroes the elements of
@@ -437,30 +430,87 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     }
   };
 
-  // Three-stage ring, two steps in flight.  Before step j: this wavefront's
-  // loads of step j are done (those of j + 1 may still run), then a barrier:
-  // every wavefront's loads of step j are in LDS and every wavefront is done
-  // reading step j - 1, whose stage the loads of step j + 2 then refill.
-  uint32_t valid[RG::kStages] = {0u, 0u, 0u};
-  if (nsteps > 0) valid[0] = issue(0, 0);
-  if (nsteps > 1) valid[1] = issue(1, 1);
-  auto step = [&](auto stage_c, int j) {
+  // Step j (stage S = j % 4): V fragments of step j from LDS, S^T with the K
+  // fragments read during the previous step, the next step's K fragments
+  // from LDS (in flight during the softmax), then P.V.  LDS reads complete in
+  // order, so "all but the newest N" waits are exact.
+  const uint32_t ka = lds0 + lane * 16, va = lds0 + lane * 8;
+  FragPair<Tag, D> f;                   // f.k: this step's K, f.v: this step's V
+  auto compute = [&](auto stage_c, int j, uint32_t valid, bool next_k) {
     constexpr int S = decltype(stage_c)::value;
-    if (j + 1 < nsteps) vm_wait<RG::kPerWave>(); else vm_wait<0>();
-    if (wave >= 2 && valid[S] != 0xffffffffu) {   // this wavefront's V loads of step j are done
-      zero_v_rows(S, valid[S]);
+    constexpr int S1 = (S + 1) % RG::kStages;
+    read_v<S * RG::kStep + RG::kKBytes>(f, va, std::make_integer_sequence<int, D / 16>());
+    lgkm_wait<D / 16>();                // this step's K (read before V) arrived
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < RG::kChunks; ++m) reg_after(f.k[h][m]);
+    f32x4 sa[NQ], sb[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], sa[q], sb[q]);
+    if (next_k) {
+      read_k<S1 * RG::kStep>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
+      lgkm_wait<2 * RG::kChunks>();     // V arrived; the next K may still be in flight
+    } else {
+      lgkm_wait<0>();
+    }
+#pragma unroll
+    for (int d = 0; d < D / 16; ++d) reg_after(f.v[d]);
+    const int key0 = 32 * j;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      softmax_pv<Tag, D>(f, sa[q], sb[q], st[q], valid, a.qk_scale, lane, pos[q] - key0 + 1);
+  };
+
+  // Four-stage ring.  Loads run three steps ahead of the computation: at
+  // step j the stage of step j - 1 (all of its reads done, by the barrier)
+  // takes the loads of step j + 3.  Before the barrier of step j this
+  // wavefront's loads of step j + 1 are done (those of j + 2 may still run),
+  // so after it every wavefront may read step j + 1's K.
+  uint32_t valid[RG::kStages] = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < 3 && i < nsteps; ++i) {
+    const Prep pr = prepare(i);
+    valid[i] = pr.valid;
+    dma(pr, i);
+  }
+  if (nsteps > 0) {
+    if (nsteps > 2) vm_wait<2 * RG::kPerWave>(); else if (nsteps > 1) vm_wait<RG::kPerWave>(); else vm_wait<0>();
+    if (wave >= 2 && valid[0] != 0xffffffffu) {
+      zero_v_rows(0, valid[0]);
       lgkm_wait<0>();
     }
     __builtin_amdgcn_s_barrier();
-    if (j + 2 < nsteps) valid[(S + 2) % 3] = issue(j + 2, (S + 2) % 3);
-    if (32 * j <= p_wave) compute(stage_c, j, valid[S]);
+    read_k<0>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
+  }
+  auto step = [&](auto stage_c, int j) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int S1 = (S + 1) % RG::kStages;
+    constexpr int S3 = (S + 3) % RG::kStages;
+    Prep pr;
+    const bool more = j + 3 < nsteps;
+    if (more) pr = prepare(j + 3);
+    if (j + 1 < nsteps) {
+      if (j + 2 < nsteps) vm_wait<RG::kPerWave>(); else vm_wait<0>();
+      if (wave >= 2 && valid[S1] != 0xffffffffu) {   // this wavefront's V loads of step j + 1 are done
+        zero_v_rows(S1, valid[S1]);
+        lgkm_wait<0>();
+      }
+    }
+    __builtin_amdgcn_s_barrier();
+    if (more) {
+      valid[S3] = pr.valid;
+      dma(pr, S3);
+    }
+    compute(stage_c, j, valid[S], j + 1 < nsteps);
   };
-  for (int j = 0; j < nsteps; j += 3) {
+  for (int j = 0; j < nsteps; j += 4) {
     step(std::integral_constant<int, 0>(), j);
     if (j + 1 >= nsteps) break;
     step(std::integral_constant<int, 1>(), j + 1);
     if (j + 2 >= nsteps) break;
     step(std::integral_constant<int, 2>(), j + 2);
+    if (j + 3 >= nsteps) break;
+    step(std::integral_constant<int, 3>(), j + 3);
   }
 
 #pragma unroll
