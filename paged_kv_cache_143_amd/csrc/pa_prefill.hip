@@ -86,68 +86,69 @@ __device__ inline void qk_pair(const FragPair<Tag, D>& f, const QFrag<Tag, D>& q
   }
 }
 
-// Online softmax and O^T += V^T P^T for one column group, from its scores.
-// valid: bit k set when key k of the step is stored (wave-uniform); lima: per
-// lane, the column's causal limit in rows of tile a (>= 32: the whole step is
-// visible; tile b's limit is lima - 16); c = scale * log2(e).  V rows of
-// invalid keys must already be zero.  The exponentials are taken against the
-// current base first and checked afterwards: only when one exceeds 2^8 (or
-// overflows), or the column has no base yet, does the wavefront move the
-// base to the running maximum, rescale l and acc, and take them again -- the
-// same softmax for any base, and no maximum of the scores on the common
-// path.  p >= 0, so its largest value is an integer maximum of the bit
-// patterns.
-template <class Tag, int D>
-__device__ inline void softmax_pv(const FragPair<Tag, D>& f, f32x4 sa, f32x4 sb, State<D>& st,
-                                  uint32_t valid, float c, int lane, int lima) {
-  const float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+// Online softmax of one column group over one step, in stages that let the
+// scheduler overlap one group's (or step's) vector work with matrix
+// products of another.  c = scale * log2(e).
+//
+// mask_scores: scores of invalid keys (bit k of `valid` clear: a tail past L
+// or a block outside the pool) or of keys past the column's causal limit
+// become -inf * sign(c), so that c * s = -inf (a select: such rows may hold
+// NaN).  lima: per lane, the column's causal limit in rows of tile a (tile
+// b's is lima - 16).
+template <int D>
+__device__ inline void mask_scores(f32x4& sa, f32x4& sb, uint32_t valid, float c, int lane, int lima) {
+  const float ninf = c >= 0.f ? -INFINITY : INFINITY;
+  const int t0 = 4 * (lane >> 4);
+  const uint32_t ma = valid >> t0, mb = valid >> (16 + t0);
   const int limb = lima - kRows;
-  const bool masked = valid != 0xffffffffu || __builtin_amdgcn_ballot_w64(limb < kRows) != 0;
-  float x[8];                 // exponent arguments before the base: c s, or -inf when masked
-  if (masked) {
-    const int t0 = 4 * (lane >> 4);
-    const uint32_t ma = valid >> t0, mb = valid >> (16 + t0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // select, never multiply: invalid rows may hold NaN
-      x[r] = ((ma >> r) & 1u) && t0 + r < lima ? s[r] * c : -INFINITY;
-      x[4 + r] = ((mb >> r) & 1u) && t0 + r < limb ? s[4 + r] * c : -INFINITY;
-    }
+  for (int r = 0; r < 4; ++r) {
+    sa[r] = ((ma >> r) & 1u) && t0 + r < lima ? sa[r] : ninf;
+    sb[r] = ((mb >> r) & 1u) && t0 + r < limb ? sb[r] : ninf;
   }
-  float p[8];
-  auto exps = [&]() {
-    const float base = st.m == -INFINITY ? 0.f : st.m;
-    if (masked) {
+}
+
+// p = exp2(c s - base) against the column's current base (0 while it has
+// none); returns whether the column needs the exact path: some p > 2^8
+// (= 256.0f; p >= 0, so an integer maximum of the bit patterns finds it) or
+// no base yet.
+template <int D>
+__device__ inline bool take_exps(f32x4 sa, f32x4 sb, const State<D>& st, float c, float* p) {
+  const float base = st.m == -INFINITY ? 0.f : st.m;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) p[r] = fast_exp2(x[r] - base);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], c, -base));
-    }
-  };
-  exps();
-  const uint32_t pm = max(max(max(__float_as_uint(p[0]), __float_as_uint(p[1])), max(__float_as_uint(p[2]), __float_as_uint(p[3]))),
-           max(max(__float_as_uint(p[4]), __float_as_uint(p[5])), max(__float_as_uint(p[6]), __float_as_uint(p[7]))));
-  // Some p > 2^8 (= 256.0f), or a column still without a base (m = -inf:
-  // the exponentials above used base 0 only provisionally).
-  if (__builtin_amdgcn_ballot_w64(pm > 0x43800000u || st.m == -INFINITY) != 0) {
-    float bm = -INFINITY;
-    if (masked) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) bm = fmaxf(bm, x[r]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) bm = fmaxf(bm, s[r] * c);
-    }
-    bm = xor_max(bm);
-    const float m_new = fmaxf(st.m, bm);
-    const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.f : m_new));
-    st.l *= alpha;
-#pragma unroll
-    for (int n = 0; n < D / 16; ++n) st.acc[n] *= alpha;
-    st.m = m_new;
-    exps();
+  for (int r = 0; r < 4; ++r) {
+    p[r] = fast_exp2(__builtin_fmaf(sa[r], c, -base));
+    p[4 + r] = fast_exp2(__builtin_fmaf(sb[r], c, -base));
   }
+  const uint32_t pm = max(max(max(__float_as_uint(p[0]), __float_as_uint(p[1])),
+                              max(__float_as_uint(p[2]), __float_as_uint(p[3]))),
+                          max(max(__float_as_uint(p[4]), __float_as_uint(p[5])),
+                              max(__float_as_uint(p[6]), __float_as_uint(p[7]))));
+  return pm > 0x43800000u || st.m == -INFINITY;
+}
+
+// The exact path (rare): move the base to the running maximum, rescale l and
+// acc, and take the exponentials again -- the same softmax for any base.
+template <int D>
+__device__ inline void rebase(f32x4 sa, f32x4 sb, State<D>& st, float c, float* p) {
+  float bm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bm = fmaxf(bm, fmaxf(sa[r] * c, sb[r] * c));
+  bm = xor_max(bm);
+  const float m_new = fmaxf(st.m, bm);
+  const float alpha = fast_exp2(st.m - (m_new == -INFINITY ? 0.f : m_new));
+  st.l *= alpha;
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) st.acc[n] *= alpha;
+  st.m = m_new;
+  take_exps<D>(sa, sb, st, c, p);
+}
+
+// l += sum p; acc += V^T P^T with P split into high and low 16-bit parts
+// (two products with the same V fragment).  V rows of invalid keys must be
+// zero (their p is 0, but 0 * NaN is NaN).
+template <class Tag, int D>
+__device__ inline void accumulate(const FragPair<Tag, D>& f, const float* p, State<D>& st) {
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   u32x4 hi, lo;
 #pragma unroll
@@ -430,36 +431,58 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     }
   };
 
-  // Step j (stage S = j % 4): V fragments of step j from LDS, S^T with the K
-  // fragments read during the previous step, the next step's K fragments
-  // from LDS (in flight during the softmax), then P.V.  LDS reads complete in
-  // order, so "all but the newest N" waits are exact.
+  // Step j (stage S = j % 4), software-pipelined across steps: the scores
+  // S^T of step j were computed during step j - 1.  Read V of step j and K of
+  // step j + 1 from LDS; mask step j's scores where needed; take the
+  // exponentials of step j while the matrix cores compute step j + 1's
+  // scores; then P.V of step j, whose products overlap the narrowing of P.
+  // LDS reads complete in order.  On the last step the next stage holds no
+  // step (stale or never written LDS): its scores are computed and unused,
+  // which keeps the step free of branches.
   const uint32_t ka = lds0 + lane * 16, va = lds0 + lane * 8;
-  FragPair<Tag, D> f;                   // f.k: this step's K, f.v: this step's V
-  auto compute = [&](auto stage_c, int j, uint32_t valid, bool next_k) {
+  FragPair<Tag, D> f;                   // f.k: next step's K, f.v: this step's V
+  f32x4 sa[NQ], sb[NQ];                 // this step's scores
+  auto scores = [&](f32x4* xa, f32x4* xb) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], xa[q], xb[q]);
+  };
+  auto compute = [&](auto stage_c, int j, uint32_t valid) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int S1 = (S + 1) % RG::kStages;
     read_v<S * RG::kStep + RG::kKBytes>(f, va, std::make_integer_sequence<int, D / 16>());
-    lgkm_wait<D / 16>();                // this step's K (read before V) arrived
+    read_k<S1 * RG::kStep>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
+    const int key0 = 32 * j;
+    bool need = valid != 0xffffffffu;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) need |= __builtin_amdgcn_ballot_w64(pos[q] - key0 + 1 < 2 * kRows) != 0;
+    if (need) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) mask_scores<D>(sa[q], sb[q], valid, a.qk_scale, lane, pos[q] - key0 + 1);
+    }
+    float p[NQ][8];
+    bool fix = false;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) fix |= take_exps<D>(sa[q], sb[q], st[q], a.qk_scale, p[q]);
+    lgkm_wait<0>();                     // V of this step and K of the next
+#pragma unroll
+    for (int d = 0; d < D / 16; ++d) reg_after(f.v[d]);
+    f32x4 na[NQ], nb[NQ];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int m = 0; m < RG::kChunks; ++m) reg_after(f.k[h][m]);
-    f32x4 sa[NQ], sb[NQ];
+    scores(na, nb);
+    if (__builtin_amdgcn_ballot_w64(fix) != 0) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], sa[q], sb[q]);
-    if (next_k) {
-      read_k<S1 * RG::kStep>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
-      lgkm_wait<2 * RG::kChunks>();     // V arrived; the next K may still be in flight
-    } else {
-      lgkm_wait<0>();
+      for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], a.qk_scale, p[q]);
     }
 #pragma unroll
-    for (int d = 0; d < D / 16; ++d) reg_after(f.v[d]);
-    const int key0 = 32 * j;
+    for (int q = 0; q < NQ; ++q) accumulate<Tag, D>(f, p[q], st[q]);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      softmax_pv<Tag, D>(f, sa[q], sb[q], st[q], valid, a.qk_scale, lane, pos[q] - key0 + 1);
+    for (int q = 0; q < NQ; ++q) {
+      sa[q] = na[q];
+      sb[q] = nb[q];
+    }
   };
 
   // Four-stage ring.  Loads run three steps ahead of the computation: at
@@ -481,6 +504,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     }
     __builtin_amdgcn_s_barrier();
     read_k<0>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
+    lgkm_wait<0>();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < RG::kChunks; ++m) reg_after(f.k[h][m]);
+    scores(sa, sb);
   }
   auto step = [&](auto stage_c, int j) {
     constexpr int S = decltype(stage_c)::value;
@@ -501,7 +530,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
       valid[S3] = pr.valid;
       dma(pr, S3);
     }
-    compute(stage_c, j, valid[S], j + 1 < nsteps);
+    compute(stage_c, j, valid[S]);
   };
   for (int j = 0; j < nsteps; j += 4) {
     step(std::integral_constant<int, 0>(), j);
@@ -737,6 +766,9 @@ pa_status pa_prefill_attention(const pa_pool_desc* pool, const void* k_pool, con
   const int32_t wg_rows = kPWaves * a.wave_rows;
   a.num_tiles = (max_chunk_len + wg_rows - 1) / wg_rows;
   a.qk_scale = scale * 1.4426950408889634f;
+  // A zero scale becomes the smallest normal float: every exponential is still
+  // exactly 1, and a masked score (-inf) still gives -inf rather than NaN.
+  if (a.qk_scale == 0.f) a.qk_scale = 1.17549435e-38f;
   a.k_scales = pool->k_scales;
   a.v_scales = pool->v_scales;
   const int64_t pairs = (int64_t)a.num_kv_heads * num_seqs;
