@@ -214,11 +214,15 @@ struct PrefillArgs {
 //     at dim 16n + lane % 16 -- both tiles' B halves, one ds_read2st64_b64.
 // The loading lanes gather these from the pool layout (include/pa.h): K
 // sub-tile [d/32][R][32] and V sub-tile [R/4][d][4], R = min(b, 16).
+#ifndef PA_RING_STAGES
+#define PA_RING_STAGES 4
+#endif
 template <int D> struct Ring {
   static constexpr int kChunks = D / 32;                  // K chunks per tile
   static constexpr int kKBytes = 2 * kChunks * 1024;
   static constexpr int kStep = kKBytes + (D / 16) * 1024;
-  static constexpr int kStages = 4;
+  static constexpr int kStages = PA_RING_STAGES;
+  static constexpr int kAhead = kStages - 1;                // steps loaded ahead
   static constexpr int kPerWave = kStep / 1024 / kPWaves;  // load instructions per step
   static_assert(kPerWave == kChunks, "waves 0-1 load K, waves 2-3 load V");
 };
@@ -485,19 +489,27 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     }
   };
 
-  // Four-stage ring.  Loads run three steps ahead of the computation: at
-  // step j the stage of step j - 1 (all of its reads done, by the barrier)
-  // takes the loads of step j + 3.  Before the barrier of step j this
-  // wavefront's loads of step j + 1 are done (those of j + 2 may still run),
-  // so after it every wavefront may read step j + 1's K.
-  uint32_t valid[RG::kStages] = {0u, 0u, 0u, 0u};
-  for (int i = 0; i < 3 && i < nsteps; ++i) {
+  // Ring of kStages stages; loads run kAhead = kStages - 1 steps ahead of the
+  // computation: at step j the stage of step j - 1 (all of its reads done,
+  // by the barrier) takes the loads of step j + kAhead.  Before the barrier
+  // of step j this wavefront's loads of step j + 1 are done (later steps' may
+  // still run), so after it every wavefront may read step j + 1's K.
+  // vm_steps(k): wait until at most k steps' loads of this wavefront are
+  // outstanding.
+  auto vm_steps = [](int k) {
+    if (k >= 2) vm_wait<2 * RG::kPerWave>(); else if (k == 1) vm_wait<RG::kPerWave>(); else vm_wait<0>();
+  };
+  static_assert(RG::kAhead <= 3, "vm_steps covers up to two newer steps");
+  uint32_t valid[RG::kStages];
+#pragma unroll
+  for (int i = 0; i < RG::kStages; ++i) valid[i] = 0u;
+  for (int i = 0; i < RG::kAhead && i < nsteps; ++i) {
     const Prep pr = prepare(i);
     valid[i] = pr.valid;
     dma(pr, i);
   }
   if (nsteps > 0) {
-    if (nsteps > 2) vm_wait<2 * RG::kPerWave>(); else if (nsteps > 1) vm_wait<RG::kPerWave>(); else vm_wait<0>();
+    vm_steps(min(RG::kAhead, nsteps) - 1);
     if (wave >= 2 && valid[0] != 0xffffffffu) {
       zero_v_rows(0, valid[0]);
       lgkm_wait<0>();
@@ -514,12 +526,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   auto step = [&](auto stage_c, int j) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int S1 = (S + 1) % RG::kStages;
-    constexpr int S3 = (S + 3) % RG::kStages;
+    constexpr int SA = (S + RG::kAhead) % RG::kStages;
     Prep pr;
-    const bool more = j + 3 < nsteps;
-    if (more) pr = prepare(j + 3);
+    const bool more = j + RG::kAhead < nsteps;
+    if (more) pr = prepare(j + RG::kAhead);
     if (j + 1 < nsteps) {
-      if (j + 2 < nsteps) vm_wait<RG::kPerWave>(); else vm_wait<0>();
+      vm_steps(min(RG::kAhead - 2, nsteps - j - 2));
       if (wave >= 2 && valid[S1] != 0xffffffffu) {   // this wavefront's V loads of step j + 1 are done
         zero_v_rows(S1, valid[S1]);
         lgkm_wait<0>();
@@ -527,19 +539,21 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     }
     __builtin_amdgcn_s_barrier();
     if (more) {
-      valid[S3] = pr.valid;
-      dma(pr, S3);
+      valid[SA] = pr.valid;
+      dma(pr, SA);
     }
     compute(stage_c, j, valid[S]);
   };
-  for (int j = 0; j < nsteps; j += 4) {
+  for (int j = 0; j < nsteps; j += RG::kStages) {
     step(std::integral_constant<int, 0>(), j);
     if (j + 1 >= nsteps) break;
     step(std::integral_constant<int, 1>(), j + 1);
     if (j + 2 >= nsteps) break;
     step(std::integral_constant<int, 2>(), j + 2);
-    if (j + 3 >= nsteps) break;
-    step(std::integral_constant<int, 3>(), j + 3);
+    if constexpr (RG::kStages > 3) {
+      if (j + 3 >= nsteps) break;
+      step(std::integral_constant<int, 3 % RG::kStages>(), j + 3);
+    }
   }
 
 #pragma unroll
