@@ -38,7 +38,8 @@ KERNEL_SOURCES = ("paged_kv_cache_143_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_143_amd/csrc/pa_tile.h",
                   "paged_kv_cache_143_amd/csrc/pa_internal.h")
 PCIE_PEAK_GBS = 64.0            # host link: PCIe 5.0 x16, one direction, published
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # dense, published
+# dense, published; FP8 caches are computed on bf16 matrix cores (codes widened in registers)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 2500.0, "f32": 157.3}
 
 
 # name -> (constructor, default partition size, length description, headline?)
@@ -63,6 +64,7 @@ def _workloads():
         "swap-gqa-bf16": (W.swap_gqa_bf16, 0,
                           "uniform int 200..2000; every third sequence swapped out and back"),
         "prefill-bf16": (W.prefill_bf16, 0, "16 prompts x 2048 tokens, no cached prefix"),
+        "prefill-fp8": (W.prefill_fp8, 0, "16 prompts x 2048 tokens, no cached prefix, FP8 E4M3 cache"),
         "chunked-prefill-bf16": (W.chunked_prefill_bf16, 0,
                                  "32 x 512-token chunks over cached prefixes U{512..4096}"),
     }

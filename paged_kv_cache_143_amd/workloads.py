@@ -342,6 +342,12 @@ def prefill_bf16(num_seqs: int = 16, prompt_len: int = 2048, seed: int = 6) -> W
                    32, 8, 128)
 
 
+def prefill_fp8(num_seqs: int = 16, prompt_len: int = 2048, seed: int = 6) -> Workload:
+    """The whole-prompt prefill workload (same prompts and values) on an FP8 E4M3 cache."""
+    return chunked("prefill-fp8", seed, "fp8", [0] * num_seqs, [prompt_len] * num_seqs,
+                   32, 8, 128)
+
+
 def chunked_prefill_bf16(num_seqs: int = 32, chunk: int = 512, seed: int = 7) -> Workload:
     """Chunked prefill: 32 sequences with cached prefixes U{512..4096} and a
     512-token chunk each (a 16K-token step), 32 q / 8 kv heads x 128, bf16."""
