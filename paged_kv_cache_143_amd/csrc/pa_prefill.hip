@@ -217,14 +217,21 @@ struct PrefillArgs {
 #ifndef PA_RING_STAGES
 #define PA_RING_STAGES 4
 #endif
-template <int D> struct Ring {
-  static constexpr int kChunks = D / 32;                  // K chunks per tile
-  static constexpr int kKBytes = 2 * kChunks * 1024;
-  static constexpr int kStep = kKBytes + (D / 16) * 1024;
-  static constexpr int kStages = PA_RING_STAGES;
-  static constexpr int kAhead = kStages - 1;                // steps loaded ahead
-  static constexpr int kPerWave = kStep / 1024 / kPWaves;  // load instructions per step
-  static_assert(kPerWave == kChunks, "waves 0-1 load K, waves 2-3 load V");
+template <class Tag, int D> struct Ring {
+  static constexpr bool kF8 = IsFP8<Tag>::value;
+  static constexpr int kChunks = D / 32;                  // 16-bit K chunks per tile
+  static constexpr int kKBytes = 2 * kChunks * 1024;      // 16-bit layout: K of both tiles
+  static constexpr int kStep = kKBytes + (D / 16) * 1024; // 16-bit layout: one step
+  // FP8: the loads land raw codes (half the bytes) in stages of kRawStep,
+  // converted to the 16-bit layout in slots of kStep; three of each.
+  static constexpr int kRawChunks = D / 64;               // FP8 pieces per tile, K or V
+  static constexpr int kRawStep = kStep / 2;
+  static constexpr int kStages = kF8 ? 3 : PA_RING_STAGES;
+  static constexpr int kAhead = kStages - 1;               // steps loaded ahead
+  static constexpr int kRawBase = kStages * kStep;          // FP8 raw stages after the slots
+  static constexpr int kBytes = kStages * kStep + (kF8 ? kStages * kRawStep : 0);
+  static constexpr int kPerWave = (kF8 ? kRawStep : kStep) / 1024 / kPWaves;  // loads per step
+  static_assert(kPerWave == (kF8 ? kRawChunks : kChunks), "waves 0-1 load K, waves 2-3 load V");
 };
 
 typedef const __attribute__((address_space(1))) char* gchar;
@@ -264,8 +271,11 @@ __device__ inline void read_v(FragPair<Tag, D>& f, uint32_t va, std::integer_seq
 
 template <class Tag, int D, int NQ, class OutT>
 __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) {
-  using RG = Ring<D>;
-  __shared__ __attribute__((aligned(1024))) char ring[RG::kStages * RG::kStep];
+  using RG = Ring<Tag, D>;
+  using CT = typename ComputeTag<Tag>::type;   // FP8 codes become bf16 in the slots
+  constexpr bool F8 = RG::kF8;
+  constexpr int ES = Elt<Tag>::bytes;
+  __shared__ __attribute__((aligned(1024))) char ring[RG::kBytes];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
@@ -312,6 +322,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     const int64_t qrow = has[q] ? ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) : 0;
     qf[q].load(a.q + qrow * D * 2, has[q], lane);
   }
+  // FP8: the head's K scale folds into the score scale, its V scale into the
+  // output (a zero product becomes the smallest normal float, as on the host).
+  float qk_scale = a.qk_scale;
+  float v_scale = 1.f;
+  if constexpr (F8) {
+    qk_scale *= a.k_scales[g];
+    if (qk_scale == 0.f) qk_scale = 1.17549435e-38f;
+    v_scale = a.v_scales[g];
+  }
   State<D> st[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -329,26 +348,48 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   const int R = a.rows;
   const int r_shift = R == 8 ? 3 : 4;
   const int b_shift = a.block_size == 8 ? 3 : a.block_size == 16 ? 4 : 5;
-  const int64_t tile_bytes = (int64_t)a.block_size * D * 2;
-  const int sub_bytes = R * D * 2;
+  const int64_t tile_bytes = (int64_t)a.block_size * D * ES;
+  const int sub_bytes = R * D * ES;
   const uint32_t block_stride = (uint32_t)(a.num_kv_heads * tile_bytes);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lchar)ring;
 
-  // Each lane's part of a step's loads, fixed for the whole walk: wavefront
-  // h < 2 loads K of tile h, lane (t, piece) = (lane % 16, lane / 16);
-  // wavefronts 2-3 load V, lane (tile, token group, dim pair) = (lane / 32,
-  // (lane / 8) % 4, lane % 8).  The lane's rows lie in quarter qi (keys
-  // 8 qi .. 8 qi + 7 of the step), in block qblk counted from the step's
-  // first block (a step starts on a block boundary), at byte offset
-  // lane_off inside that block's tile of this KV head.
-  const int qi = wave < 2 ? 2 * wave + ((lane >> 3) & 1) : (lane >> 4) & 3;
+  // Each lane's part of a step's loads, fixed for the whole walk.  16-bit
+  // pools: wavefront h < 2 loads K of tile h, lane (t, piece) = (lane % 16,
+  // lane / 16); wavefronts 2-3 load V, lane (tile, token group, dim pair) =
+  // (lane / 32, (lane / 8) % 4, lane % 8).  FP8 pools (raw codes, the pool's
+  // own per-lane pieces, include/pa.h): wavefront h < 2 loads K of tile h,
+  // lane (row, dim quarter) = (lane % 16, lane / 16); wavefront 2 + h loads V
+  // of tile h, lane (dim row, token group) = (lane % 16, lane / 16).  The
+  // lane's rows lie in quarter qi (keys 8 qi .. 8 qi + 7 of the step), in
+  // block qblk counted from the step's first block (a step starts on a block
+  // boundary), at byte offset lane_off inside that block's tile of this KV
+  // head; instruction i adds i * inst_stride.
+  int qi;
+  if constexpr (F8) qi = wave < 2 ? 2 * wave + ((lane >> 3) & 1) : 2 * (wave - 2) + (lane >> 5);
+  else qi = wave < 2 ? 2 * wave + ((lane >> 3) & 1) : (lane >> 4) & 3;
   const int in_blk = (8 * qi) & (a.block_size - 1);
   const int qblk = (8 * qi) >> b_shift;
   const int row_q = in_blk & (R - 1);
-  const uint32_t lane_off =
-      (uint32_t)((in_blk >> r_shift) * sub_bytes) +
-      (wave < 2 ? (uint32_t)((row_q + (lane & 7)) * 64 + (lane >> 4) * 16)
-                : (uint32_t)(((row_q >> 2) + ((lane >> 3) & 1)) * D * 8 + (lane & 7) * 16));
+  uint32_t lane_off = (uint32_t)((in_blk >> r_shift) * sub_bytes);
+  uint32_t inst_stride;
+  if constexpr (F8) {
+    if (wave < 2) {
+      lane_off += (uint32_t)((row_q + (lane & 7)) * 16 + (lane >> 4) * (R * D / 4));
+      inst_stride = (uint32_t)(R * 16);
+    } else {
+      lane_off += (uint32_t)(((row_q >> 2) + ((lane >> 4) & 1)) * 4 * D + (lane & 15) * 16);
+      inst_stride = 256u;
+    }
+  } else {
+    if (wave < 2) {
+      lane_off += (uint32_t)((row_q + (lane & 7)) * 64 + (lane >> 4) * 16);
+      inst_stride = (uint32_t)(R * 64);
+    } else {
+      lane_off += (uint32_t)(((row_q >> 2) + ((lane >> 3) & 1)) * D * 8 + (lane & 7) * 16 +
+                             (wave - 2) * RG::kChunks * 128);   // first dim tile of this wavefront
+      inst_stride = 128u;
+    }
+  }
   const uint64_t lane_base = (wave < 2 ? (uint64_t)a.k_pool : (uint64_t)a.v_pool) +
                              (uint64_t)((int64_t)g * tile_bytes) + lane_off;
 
@@ -399,39 +440,73 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     }
     return pr;
   };
+  // Destination chunk of this wavefront's instruction i in a stage:
+  // 16-bit K (h, m) -> h * kChunks + m, V dim tile n -> kKBytes / 1024 + n;
+  // FP8 raw K (h, piece) -> h * kRawChunks + piece, V -> 2 kRawChunks + ...
   auto dma = [&](const Prep& pr, int stg) {
-    const uint32_t dst = lds0 + stg * RG::kStep;
-    if (wave < 2) {
+    const uint32_t dst = lds0 + (F8 ? RG::kRawBase + stg * RG::kRawStep : stg * RG::kStep);
+    const int c0 = wave * RG::kPerWave;
 #pragma unroll
-      for (int m = 0; m < RG::kChunks; ++m)
-        __builtin_amdgcn_global_load_lds((gchar)(pr.src + (uint32_t)(m * R * 64)),
-                                         (lchar)(uintptr_t)(dst + (wave * RG::kChunks + m) * 1024),
-                                         16, 0, 0);
-    } else {
-      const int n0 = (wave - 2) * RG::kChunks;
-#pragma unroll
-      for (int i = 0; i < RG::kChunks; ++i)
-        __builtin_amdgcn_global_load_lds((gchar)(pr.src + (uint32_t)((n0 + i) * 128)),
-                                         (lchar)(uintptr_t)(dst + RG::kKBytes + (n0 + i) * 1024),
-                                         16, 0, 0);
-    }
+    for (int i = 0; i < RG::kPerWave; ++i)
+      __builtin_amdgcn_global_load_lds((gchar)(pr.src + (uint32_t)(i * inst_stride)),
+                                       (lchar)(uintptr_t)(dst + (c0 + i) * 1024), 16, 0, 0);
   };
 
-  // On a step with invalid keys, each V-loading lane zeroes the elements of
-  // those keys in the pieces it loaded (a tail past L or a block outside the
-  // pool may hold NaN, and 0 * NaN would reach the accumulators).  Piece
-  // (lane, chunk n) holds tokens 4 tg .. 4 tg + 3 of tile h, two dims.
-  auto zero_v_rows = [&](int stg, uint32_t valid) {
-    const uint32_t bits = valid >> (16 * (lane >> 5) + 4 * ((lane >> 3) & 3));
-    const uint32_t k0 = (bits & 1u ? 0x0000ffffu : 0u) | (bits & 2u ? 0xffff0000u : 0u);
-    const uint32_t k1 = (bits & 4u ? 0x0000ffffu : 0u) | (bits & 8u ? 0xffff0000u : 0u);
-    const int n0 = (wave - 2) * RG::kChunks;
+  // Landing of step j's loads in stage stg, by each lane for the pieces it
+  // loaded, once its own loads of that step are done (before the barrier
+  // that publishes the stage).  16-bit pools: on a step with invalid keys the
+  // V-loading lanes zero those keys' elements (a tail past L or a block
+  // outside the pool may hold NaN, and 0 * NaN would reach the accumulators).
+  // FP8 pools: every lane widens its raw codes to the bf16 fragments of the
+  // stage's 16-bit slot (exact: every E4M3 value is a bf16 value), V with the
+  // same zeroing.  V piece of lane (d, tg) holds tokens 4 tg .. 4 tg + 3.
+  auto v_keep = [&](uint32_t valid, int tile, uint32_t& k0, uint32_t& k1) {
+    const uint32_t bits = valid >> (16 * tile + 4 * (F8 ? lane >> 4 : (lane >> 3) & 3));
+    k0 = (bits & 1u ? 0x0000ffffu : 0u) | (bits & 2u ? 0xffff0000u : 0u);
+    k1 = (bits & 4u ? 0x0000ffffu : 0u) | (bits & 8u ? 0xffff0000u : 0u);
+  };
+  auto land = [&](int stg, uint32_t valid) {
+    if constexpr (F8) {
+      const char* raw = ring + RG::kRawBase + stg * RG::kRawStep;
+      char* slot = ring + stg * RG::kStep;
+      if (wave < 2) {                   // K of tile `wave`: piece p -> fragments m = 2p, 2p + 1
 #pragma unroll
-    for (int i = 0; i < RG::kChunks; ++i) {
-      u32x4* piece = reinterpret_cast<u32x4*>(ring + stg * RG::kStep + RG::kKBytes +
-                                              (n0 + i) * 1024 + lane * 16);
-      const u32x4 x = *piece;
-      *piece = u32x4{x[0] & k0, x[1] & k1, x[2] & k0, x[3] & k1};
+        for (int pc = 0; pc < RG::kRawChunks; ++pc) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(raw + (wave * RG::kRawChunks + pc) * 1024 + lane * 16);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            *reinterpret_cast<u32x4*>(slot + (wave * RG::kChunks + 2 * pc + u) * 1024 + lane * 16) =
+                u32x4{fp8x2_to_bf16x2<false>(x[2 * u]), fp8x2_to_bf16x2<true>(x[2 * u]),
+                      fp8x2_to_bf16x2<false>(x[2 * u + 1]), fp8x2_to_bf16x2<true>(x[2 * u + 1])};
+        }
+      } else {                          // V of tile h: dword e of piece p is dim tile 4p + e
+        const int h = wave - 2;
+        uint32_t k0 = 0xffffffffu, k1 = 0xffffffffu;
+        if (valid != 0xffffffffu) v_keep(valid, h, k0, k1);
+#pragma unroll
+        for (int pc = 0; pc < RG::kRawChunks; ++pc) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(raw + (wave * RG::kRawChunks + pc) * 1024 + lane * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<u32x2*>(slot + RG::kKBytes + (4 * pc + e) * 1024 + h * 512 + lane * 8) =
+                u32x2{fp8x2_to_bf16x2<false>(x[e]) & k0, fp8x2_to_bf16x2<true>(x[e]) & k1};
+        }
+      }
+      lgkm_wait<0>();
+    } else {
+      if (wave >= 2 && valid != 0xffffffffu) {
+        uint32_t k0, k1;
+        v_keep(valid, lane >> 5, k0, k1);
+        const int n0 = (wave - 2) * RG::kChunks;
+#pragma unroll
+        for (int i = 0; i < RG::kChunks; ++i) {
+          u32x4* piece = reinterpret_cast<u32x4*>(ring + stg * RG::kStep + RG::kKBytes +
+                                                  (n0 + i) * 1024 + lane * 16);
+          const u32x4 x = *piece;
+          *piece = u32x4{x[0] & k0, x[1] & k1, x[2] & k0, x[3] & k1};
+        }
+        lgkm_wait<0>();
+      }
     }
   };
 
@@ -444,11 +519,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   // step (stale or never written LDS): its scores are computed and unused,
   // which keeps the step free of branches.
   const uint32_t ka = lds0 + lane * 16, va = lds0 + lane * 8;
-  FragPair<Tag, D> f;                   // f.k: next step's K, f.v: this step's V
+  FragPair<CT, D> f;                    // f.k: next step's K, f.v: this step's V
   f32x4 sa[NQ], sb[NQ];                 // this step's scores
   auto scores = [&](f32x4* xa, f32x4* xb) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) qk_pair<Tag, D>(f, qf[q], xa[q], xb[q]);
+    for (int q = 0; q < NQ; ++q) qk_pair<CT, D>(f, qf[q], xa[q], xb[q]);
   };
   auto compute = [&](auto stage_c, int j, uint32_t valid) {
     constexpr int S = decltype(stage_c)::value;
@@ -461,12 +536,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     for (int q = 0; q < NQ; ++q) need |= __builtin_amdgcn_ballot_w64(pos[q] - key0 + 1 < 2 * kRows) != 0;
     if (need) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) mask_scores<D>(sa[q], sb[q], valid, a.qk_scale, lane, pos[q] - key0 + 1);
+      for (int q = 0; q < NQ; ++q) mask_scores<D>(sa[q], sb[q], valid, qk_scale, lane, pos[q] - key0 + 1);
     }
     float p[NQ][8];
     bool fix = false;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) fix |= take_exps<D>(sa[q], sb[q], st[q], a.qk_scale, p[q]);
+    for (int q = 0; q < NQ; ++q) fix |= take_exps<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
     lgkm_wait<0>();                     // V of this step and K of the next
 #pragma unroll
     for (int d = 0; d < D / 16; ++d) reg_after(f.v[d]);
@@ -478,10 +553,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     scores(na, nb);
     if (__builtin_amdgcn_ballot_w64(fix) != 0) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], a.qk_scale, p[q]);
+      for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
     }
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) accumulate<Tag, D>(f, p[q], st[q]);
+    for (int q = 0; q < NQ; ++q) accumulate<CT, D>(f, p[q], st[q]);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       sa[q] = na[q];
@@ -510,10 +585,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   }
   if (nsteps > 0) {
     vm_steps(min(RG::kAhead, nsteps) - 1);
-    if (wave >= 2 && valid[0] != 0xffffffffu) {
-      zero_v_rows(0, valid[0]);
-      lgkm_wait<0>();
-    }
+    land(0, valid[0]);
     __builtin_amdgcn_s_barrier();
     read_k<0>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
     lgkm_wait<0>();
@@ -532,10 +604,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     if (more) pr = prepare(j + RG::kAhead);
     if (j + 1 < nsteps) {
       vm_steps(min(RG::kAhead - 2, nsteps - j - 2));
-      if (wave >= 2 && valid[S1] != 0xffffffffu) {   // this wavefront's V loads of step j + 1 are done
-        zero_v_rows(S1, valid[S1]);
-        lgkm_wait<0>();
-      }
+      land(S1, valid[S1]);                // this wavefront's loads of step j + 1 are done
     }
     __builtin_amdgcn_s_barrier();
     if (more) {
@@ -561,7 +630,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     const float l_tot = xor_sum(st[q].l);
     const int t = row0 + q * a.tpg + cr;
     if (!(col_ok && t < row_end)) continue;
-    const float inv = (has[q] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const float inv = (has[q] && l_tot > 0.f) ? v_scale / l_tot : 0.f;
     OutT* o = reinterpret_cast<OutT*>(a.out) +
               ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) * D;
 #pragma unroll
@@ -715,7 +784,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 
 template <class Tag, int D, class OutT>
 static pa_status launch_prefill(const PrefillArgs& a, int64_t units, hipStream_t s) {
-  if constexpr (Is16<Tag>::value && !IsFP8<Tag>::value)
+  if constexpr (Is16<Tag>::value)
     prefill_ring_kernel<Tag, D, kNQ, OutT><<<(unsigned)units, kPThreads, 0, s>>>(a);
   else
     prefill_kernel<Tag, D, kNQ, OutT><<<(unsigned)units, kPThreads, 0, s>>>(a);

@@ -164,6 +164,54 @@ def test_prefill_matches_oracle():
     assert err <= 2e-3
 
 
+@pytest.mark.parametrize("b,Hq,Hkv,D", [(8, 16, 4, 128), (32, 16, 4, 128), (16, 8, 4, 64),
+                                         (16, 16, 1, 128), (8, 6, 2, 64)])
+def test_prefill_block_sizes_and_shapes(b, Hq, Hkv, D):
+    """FP8 prefill at every block size, both head dims and several groups:
+    chunks over cached prefixes with tails inside blocks."""
+    rng = np.random.default_rng(128 + b + D + Hq)
+    pre = [int(x) for x in rng.integers(0, 200, 4)]
+    chunk = [int(x) for x in rng.integers(1, 150, 4)]
+    w = W.chunked(f"f8-pre-b{b}", 128, "fp8", pre, chunk, Hq, Hkv, D, block_size=b)
+    batch = build_batch(w, drop_payload_cache=False)
+    out = PrefillStep(batch)().cpu().numpy().astype(np.float64)
+    err = row_rel_err(out, OracleRun(w).prefill())
+    announce(f"fp8 prefill b={b} {Hq}/{Hkv}x{D}: max row rel err {err:.3e}")
+    assert np.isfinite(out).all() and err <= 2e-3
+
+
+@pytest.mark.parametrize("b,bad", [(16, 2), (8, 5)])
+def test_prefill_out_of_pool_entry(b, bad):
+    """A table entry outside the pool drops that block's keys from every
+    row's softmax (FP8 cache)."""
+    from oracle import attention as OA
+    from paged_kv_cache_143_amd import binding as B
+    w = W.chunked("f8-bad", 129, "fp8", [90, 70, 40], [30, 45, 60], 16, 4, 128, block_size=b)
+    batch = build_batch(w, drop_payload_cache=False)
+    step = PrefillStep(batch)
+    step()
+    tab = batch.tables.clone()
+    tab[1, bad] = w.num_blocks + 7
+    out = torch.full_like(step.out, 7.0)
+    B.prefill_attention_t(batch.kv.desc, batch.kv.k, batch.kv.v, step.q, out, step.q_start, tab,
+                          batch.lens, w.scale, step.max_chunk, batch.max_len)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    run = OracleRun(w)
+    ref = run.prefill()
+    starts = np.concatenate([[0], np.cumsum(w.chunk_lens)])
+    q = run.chunk_q64()
+    K, V = run.logical_kv(1)
+    L, n = K.shape[0], w.chunk_lens[1]
+    for t in range(n):
+        p = L - n + t
+        keep = [k for k in range(p + 1) if not bad * b <= k < (bad + 1) * b]
+        ref[starts[1] + t] = OA.decode_sequence(q[starts[1] + t], K[keep], V[keep], w.scale)
+    err = row_rel_err(got, ref)
+    announce(f"fp8 prefill b={b} bad entry {bad}: max row rel err {err:.3e}")
+    assert np.isfinite(got).all() and err <= 2e-3
+
+
 def test_full_size_sampled():
     """The batch-256 GQA workload on an FP8 cache, in the benchmark's launch."""
     w = W.gqa_fp8()

@@ -4,10 +4,11 @@ Buffer-resource loads are bounds-checked by the hardware (a lane past the
 resource reads zero).  Two paths use plain addresses and must stay in bounds
 on their own:
 
-* the 16-bit prefill ring (pa_prefill.hip): each step's K and V are copied
-  from the pool into an LDS stage by global-to-LDS loads, one 16-byte piece
-  per lane at a per-lane offset inside one block's tile of the KV head, and
-  read back by fragment loads at fixed LDS offsets;
+* the prefill ring (pa_prefill.hip): each step's K and V are copied from the
+  pool into an LDS stage by global-to-LDS loads, one 16-byte piece per lane
+  at a per-lane offset inside one block's tile of the KV head, and read back
+  by fragment loads at fixed LDS offsets (FP8 pools: raw codes, widened to
+  bf16 fragments by the lanes that loaded them);
 * the paired 8-token decode tiles (pa_decode.hip, load_pair8).
 
 This test re-derives those lane offsets, written as in the kernels, for every
@@ -144,3 +145,101 @@ def test_decode_pair8_loads_in_bounds(D):
     for pieces, w in ((k, 16), (v, 8)):
         for blk in (0, 1):
             assert len({o + i for b, o in pieces if b == blk for i in range(w)}) == block_bytes
+
+
+def ring_dma_fp8(b, D):
+    """FP8 pools: per (wave, lane, instruction): (quarter, byte offset in the
+    block's tile, LDS byte offset in the raw stage)."""
+    R = min(b, 16)
+    r_shift = 3 if R == 8 else 4
+    sub_bytes = R * D
+    pieces = D // 64
+    out = []
+    for wave in range(WAVES):
+        for lane in range(64):
+            qi = 2 * wave + ((lane >> 3) & 1) if wave < 2 else 2 * (wave - 2) + (lane >> 5)
+            in_blk = (8 * qi) & (b - 1)
+            row_q = in_blk & (R - 1)
+            off = (in_blk >> r_shift) * sub_bytes
+            if wave < 2:
+                off += (row_q + (lane & 7)) * 16 + (lane >> 4) * (R * D // 4)
+                stride = R * 16
+            else:
+                off += ((row_q >> 2) + ((lane >> 4) & 1)) * 4 * D + (lane & 15) * 16
+                stride = 256
+            for i in range(pieces):
+                out.append((wave, lane, qi, off + i * stride, (wave * pieces + i) * 1024 + lane * 16))
+    return out
+
+
+def k8_elem(b, D, t, d):
+    """Byte of FP8 K element (token t of the block, dim d), include/pa.h."""
+    R = min(b, 16)
+    s, r = divmod(t, R)
+    return s * R * D + (d // (D // 4)) * R * D // 4 + ((d % (D // 4)) // 16) * R * 16 + r * 16 + d % 16
+
+
+def v8_elem(b, D, t, d):
+    R = min(b, 16)
+    s, r = divmod(t, R)
+    return (s * R * D + (r // 4) * 4 * D + ((d % (D // 16)) // 4) * 256 + (d // (D // 16)) * 16
+            + (d % 4) * 4 + r % 4)
+
+
+@pytest.mark.parametrize("b", [8, 16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_ring_fp8_loads_and_widening(b, D):
+    """FP8 ring: loads stay inside the tile and the raw stage, copy each key's
+    codes once, and the widening pass (each lane its own pieces) leaves the
+    bf16 slot holding the fragments of the FP8 lane roles: K chunk (h, m),
+    lane (t, g) = dims g*D/4 + 8m .. of row 16h + t; V chunk n, tile h, lane
+    (r, tg) = tokens 4tg .. of dim r*D/16 + n."""
+    tile = b * D
+    pieces = D // 64
+    raw_step = 2 * 2 * pieces * 1024
+    src = {}
+    for qi in range(4):
+        for kk in range(8):
+            key = 8 * qi + kk
+            t = ((8 * qi) & (b - 1)) + kk
+            for d in range(D):
+                src[(qi, "K", k8_elem(b, D, t, d))] = ("K", key, d)
+                src[(qi, "V", v8_elem(b, D, t, d))] = ("V", key, d)
+    raw = {}
+    for wave, lane, qi, off, lds in ring_dma_fp8(b, D):
+        assert 0 <= off and off + 16 <= tile
+        assert 0 <= lds and lds + 16 <= raw_step
+        kind = "K" if wave < 2 else "V"
+        for e in range(16):
+            assert lds + e not in raw
+            raw[lds + e] = src[(qi, kind, off + e)]
+    assert len(raw) == 2 * 32 * D
+    # widening, as in the kernel's landing pass
+    chunks = D // 32
+    kbytes = 2 * chunks * 1024
+    slot = {}
+    for wave in range(WAVES):
+        for lane in range(64):
+            for pc in range(pieces):
+                base = (wave * pieces + pc) * 1024 + lane * 16
+                if wave < 2:
+                    for u in range(2):
+                        for e in range(8):
+                            slot[(wave * chunks + 2 * pc + u) * 1024 + lane * 16 + 2 * e] = raw[base + 8 * u + e]
+                else:
+                    h = wave - 2
+                    for e4 in range(4):
+                        for tok in range(4):
+                            slot[kbytes + (4 * pc + e4) * 1024 + h * 512 + lane * 8 + 2 * tok] = raw[base + 4 * e4 + tok]
+    for h in range(2):
+        for m in range(chunks):
+            for lane in range(64):
+                t, g = lane & 15, lane >> 4
+                for e in range(8):
+                    assert slot[(h * chunks + m) * 1024 + lane * 16 + 2 * e] == ("K", 16 * h + t, g * (D // 4) + 8 * m + e)
+    for n in range(D // 16):
+        for h in range(2):
+            for lane in range(64):
+                r, tg = lane & 15, lane >> 4
+                for e in range(4):
+                    assert slot[kbytes + n * 1024 + h * 512 + lane * 8 + 2 * e] == ("V", 16 * h + 4 * tg + e, r * (D // 16) + n)
