@@ -172,24 +172,15 @@ __device__ inline uint32_t pack4_fp8(const u32x4& a, const u32x4& b, int q, floa
   return w;
 }
 
-__global__ void write_kv_fp8_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
-                                    const char* __restrict__ k_new, const char* __restrict__ v_new,
-                                    int64_t new_stride, const int32_t* __restrict__ slots,
-                                    int32_t n, int32_t num_heads, int32_t head_dim,
-                                    int32_t block_size, int64_t num_slots,
-                                    const float* __restrict__ k_scales,
-                                    const float* __restrict__ v_scales) {
+// One 16-dim chunk c of token t, head h (a thread's share of the per-token path).
+__device__ inline void write_fp8_chunk(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                       const char* __restrict__ k_new,
+                                       const char* __restrict__ v_new, int64_t new_stride,
+                                       int t, int h, int c, int32_t slot, int32_t num_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       const float* __restrict__ k_scales,
+                                       const float* __restrict__ v_scales) {
   constexpr int X = 16;
-  const int chunks = head_dim / X;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_tok = (int64_t)num_heads * chunks;
-  if (gid >= (int64_t)n * per_tok) return;
-  const int t = (int)(gid / per_tok);
-  const int rem = (int)(gid - (int64_t)t * per_tok);
-  const int h = rem / chunks;
-  const int c = rem - h * chunks;
-  const int32_t slot = slots[t];
-  if (slot < 0 || (int64_t)slot >= num_slots) return;
   const int32_t blk = slot / block_size;
   const int32_t off = slot - blk * block_size;
   const int64_t src = ((int64_t)t * new_stride + (int64_t)h * head_dim + (int64_t)c * X) * 2;
@@ -213,6 +204,106 @@ __global__ void write_kv_fp8_kernel(char* __restrict__ k_pool, char* __restrict_
     for (int j = 0; j < 4; ++j)
       vt[fp8_v_offset(off, c * X + 4 * q + j, block_size, head_dim)] = (char)((w >> (8 * j)) & 0xFFu);
   }
+}
+
+__global__ void write_kv_fp8_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                    const char* __restrict__ k_new, const char* __restrict__ v_new,
+                                    int64_t new_stride, const int32_t* __restrict__ slots,
+                                    int32_t n, int32_t num_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_slots,
+                                    const float* __restrict__ k_scales,
+                                    const float* __restrict__ v_scales) {
+  const int chunks = head_dim / 16;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tok = (int64_t)num_heads * chunks;
+  if (gid >= (int64_t)n * per_tok) return;
+  const int t = (int)(gid / per_tok);
+  const int rem = (int)(gid - (int64_t)t * per_tok);
+  const int h = rem / chunks;
+  const int c = rem - h * chunks;
+  const int32_t slot = slots[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  write_fp8_chunk(k_pool, v_pool, k_new, v_new, new_stride, t, h, c, slot, num_heads, head_dim,
+                  block_size, k_scales, v_scales);
+}
+
+// FP8 pools, 4 or more tokens: as write_kv_groups_kernel, a wavefront per 4
+// input tokens and KV head writes a run of 4 consecutive slots from a
+// multiple of 4 as whole pieces: K as head_dim / 16 runs of 64 bytes (the 4
+// rows' 16-byte pieces are adjacent), V as the token group's 4 * head_dim
+// contiguous bytes, each lane one 16-byte chunk of 4 dims x 4 tokens (no
+// byte stores).  Lanes 0 .. D/4 - 1 write K, D/4 .. D/2 - 1 write V.  Other
+// tokens are written per 16-dim chunk as above.
+__global__ __launch_bounds__(64) void write_kv_fp8_groups_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, int64_t new_stride, const int32_t* __restrict__ slots,
+    int32_t n, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_slots,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x % num_heads;
+  const int t0 = (blockIdx.x / num_heads) * 4;
+  const int D = head_dim;
+  int lead = -1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (lead < 0 && group_lead(slots, n, t0 + k, num_slots)) lead = t0 + k;
+  if (lead >= 0 && lane < D / 2) {
+    const int32_t s = slots[lead];
+    const int32_t blk = s / block_size;
+    const int32_t o = s - blk * block_size;                    // multiple of 4
+    char* kt = k_pool + ((int64_t)blk * num_heads + h) * (int64_t)block_size * D;
+    char* vt = v_pool + ((int64_t)blk * num_heads + h) * (int64_t)block_size * D;
+    if (lane < D / 4) {
+      // K: lane -> (row r of the group, 16-dim chunk c); rows of one chunk adjacent.
+      const int r = lane & 3, c = lane >> 2;
+      const int64_t src = ((int64_t)(lead + r) * new_stride + (int64_t)h * D + c * 16) * 2;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(k_new + src);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(k_new + src + 16);
+      const float ks = k_scales[h];
+      u32x4 kc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kc[q] = pack4_fp8(a, b, q, ks);
+      *reinterpret_cast<u32x4*>(kt + fp8_k_offset(o + r, c * 16, block_size, D)) = kc;
+    } else {
+      // V: chunk v of the group's 4*D bytes = (piece hh, dim row dr): dims
+      // dr*D/16 + 4hh .. +3, byte (e, j) = dim e, token j.
+      const int v = lane - D / 4;
+      const int hh = v >> 4, dr = v & 15;
+      const int d0 = dr * (D / 16) + 4 * hh;
+      const float vs = v_scales[h];
+      uint32_t w[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(
+            v_new + ((int64_t)(lead + j) * new_stride + (int64_t)h * D + d0) * 2);
+        w[j][0] = x[0];
+        w[j][1] = x[1];
+      }
+      u32x4 vc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float f = bf16_bits_to_float((w[j][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+          word |= fp8_code(f, vs) << (8 * j);
+        }
+        vc[e] = word;
+      }
+      *reinterpret_cast<u32x4*>(vt + fp8_v_offset(o, d0, block_size, D)) = vc;
+    }
+  }
+  // Tokens of t0 .. t0 + 3 outside every group: 16 lanes each, a 16-dim chunk per lane.
+  const int t = t0 + (lane >> 4);
+  const int c = lane & 15;
+  if (t >= n || c >= D / 16) return;
+  const int32_t slot = slots[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  if (lead >= 0 && t >= lead && t < lead + 4) return;           // in this wavefront's group
+  if (group_lead(slots, n, t - (slot & 3), num_slots) && slots[t - (slot & 3)] == slot - (slot & 3))
+    return;                                                     // in an earlier group
+  write_fp8_chunk(k_pool, v_pool, k_new, v_new, new_stride, t, h, c, slot, num_heads, D,
+                  block_size, k_scales, v_scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,7 +469,14 @@ pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, cons
   const int64_t blocks = (vecs + threads - 1) / threads;
   if (blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
   const int64_t num_slots = (int64_t)pool->num_blocks * pool->block_size;
-  if (es == 1)
+  if (es == 1 && n >= 4) {
+    const int64_t groups = ((int64_t)n + 3) / 4 * pool->num_kv_heads;
+    if (groups > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    write_kv_fp8_groups_kernel<<<(unsigned)groups, 64, 0, (hipStream_t)stream>>>(
+        (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
+        slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots,
+        pool->k_scales, pool->v_scales);
+  } else if (es == 1)
     write_kv_fp8_kernel<<<(unsigned)blocks, threads, 0, (hipStream_t)stream>>>(
         (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, new_stride,
         slot_mapping, n, pool->num_kv_heads, pool->head_dim, pool->block_size, num_slots,

@@ -72,6 +72,51 @@ def test_write_kv_codes_bitexact(D):
     assert_pool_equal(got_v, want_v)
 
 
+@pytest.mark.parametrize("D,b", [(128, 16), (64, 8), (128, 32), (128, 8), (64, 32)])
+def test_write_kv_runs_codes_bitexact(D, b):
+    """Many-token writes into an FP8 pool (the grouped path): runs of
+    consecutive slots starting at every offset mod 4, crossing blocks, broken
+    by skipped slots, next to lone tokens and an out-of-pool slot; every code
+    equals the oracle's, every other slot keeps its poison."""
+    rng = np.random.default_rng(13)
+    Hkv, nb = 2, 24
+    ks, vs = [0.0107, 3.5], [2.0, 0.0049]
+    kv = PagedKV(nb, Hkv, D, "fp8", poison=True, block_size=b, kv_scales=(ks, vs))
+    lens = [2 * b + 5, 3, 7, b + 6, 1, 4 * b, 9, 6]
+    gaps = [0, 2, 1, 3, 2, 2, 2, 3]
+    starts, cur = [], 0
+    for L, gap in zip(lens, gaps):
+        starts.append(cur + gap)
+        cur += gap + L
+    assert {s0 % 4 for s0 in starts} == {0, 1, 2, 3} and cur <= nb * b
+    slots = np.concatenate([np.arange(s0, s0 + L) for s0, L in zip(starts, lens)])
+    used = set(slots.tolist())
+    lone = [x for x in rng.permutation(nb * b) if x not in used][:11]
+    slots = np.concatenate([slots[:20], lone[:5], slots[20:], lone[5:]]).astype(np.int32)
+    slots[rng.choice(len(slots), 4, replace=False)] = -1
+    slots[9] = nb * b + 2
+    n = len(slots)
+    base = _crafted(n * D, rng)
+    k_new = torch.stack([base.roll(17 * h) for h in range(Hkv)], 0).view(Hkv, n, D).permute(1, 0, 2).contiguous()
+    v_new = torch.stack([base.roll(-29 * h) for h in range(Hkv)], 0).view(Hkv, n, D).permute(1, 0, 2).contiguous()
+    kv.write(k_new.cuda(), v_new.cuda(), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    got_k, got_v = pool_logical(kv, Hkv, D)
+    want_k = np.full(got_k.shape, np.nan)
+    want_v = np.full(got_v.shape, np.nan)
+    ok = (slots >= 0) & (slots < nb * b)
+    s_ok = slots[ok]
+    for h in range(Hkv):
+        ck = OF8.quantize(k_new[:, h].float().numpy(), ks[h]).astype(np.float64)[ok]
+        cv = OF8.quantize(v_new[:, h].float().numpy(), vs[h]).astype(np.float64)[ok]
+        ck[(ck == 0x7F) | (ck == 0xFF)] = np.nan
+        cv[(cv == 0x7F) | (cv == 0xFF)] = np.nan
+        want_k[s_ok // b, s_ok % b, h] = ck
+        want_v[s_ok // b, s_ok % b, h] = cv
+    assert_pool_equal(got_k, want_k)
+    assert_pool_equal(got_v, want_v)
+
+
 def _fp8(make):
     def f():
         w = make()
