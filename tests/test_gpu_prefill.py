@@ -34,7 +34,7 @@ def _gpu(request):
 
 def _poison_chunks(batch, step):
     w = batch.w
-    nan = torch.full(step.k_new.shape, float("nan"), dtype=W.DTYPES[w.dtype], device="cuda")
+    nan = torch.full(step.k_new.shape, float("nan"), dtype=step.k_new.dtype, device="cuda")
     from paged_kv_cache_143_amd import binding as B
     slots = torch.empty_like(step.slots)
     B.slot_mapping_t(batch.tables, step.seq_ids, step.positions, slots, batch.kv.block_size)
@@ -231,3 +231,18 @@ def test_zero_and_negative_scale():
         err = row_rel_err(got, ref)
         announce(f"{name} scale: max row rel err {err:.3e}")
         assert err <= 2e-3
+
+
+@pytest.mark.parametrize("b,dtype", [(8, "bf16"), (16, "f16"), (32, "bf16"), (8, "fp8")])
+def test_long_prefix_crosses_table_windows(b, dtype):
+    """Chunks over prefixes of thousands of tokens: the walk reloads its
+    64-block table window several times (at b = 8, 2900 tokens are 363
+    blocks), and chunks start at positions that are not multiples of 32."""
+    w = W.chunked(f"plong-{b}", 107, dtype, [2900, 1333, 611], [37, 64, 19], 16, 4, 128,
+                  block_size=b)
+    got, _, _ = _run(w)
+    ref = OracleRun(w).prefill()
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    announce(f"b={b} {dtype} long prefix: max row rel err {err:.3e}")
+    assert err <= 2e-3
