@@ -65,6 +65,8 @@ def _workloads():
                           "uniform int 200..2000; every third sequence swapped out and back"),
         "prefill-bf16": (W.prefill_bf16, 0, "16 prompts x 2048 tokens, no cached prefix"),
         "prefill-fp8": (W.prefill_fp8, 0, "16 prompts x 2048 tokens, no cached prefix, FP8 E4M3 cache"),
+        "prefill-opt13b-f16": (W.prefill_opt13b_f16, 0,
+                               "8 prompts x 2048 tokens, no cached prefix, 40/40 heads x 128 fp16"),
         "chunked-prefill-bf16": (W.chunked_prefill_bf16, 0,
                                  "32 x 512-token chunks over cached prefixes U{512..4096}"),
     }

@@ -348,6 +348,13 @@ def prefill_fp8(num_seqs: int = 16, prompt_len: int = 2048, seed: int = 6) -> Wo
                    32, 8, 128)
 
 
+def prefill_opt13b_f16(num_seqs: int = 8, prompt_len: int = 2048, seed: int = 8) -> Workload:
+    """OPT-13B-shaped whole-prompt prefill: 8 prompts of 2048 tokens, 40 heads
+    (MHA) x 128, fp16."""
+    return chunked("prefill-opt13b-f16", seed, "f16", [0] * num_seqs, [prompt_len] * num_seqs,
+                   40, 40, 128)
+
+
 def chunked_prefill_bf16(num_seqs: int = 32, chunk: int = 512, seed: int = 7) -> Workload:
     """Chunked prefill: 32 sequences with cached prefixes U{512..4096} and a
     512-token chunk each (a 16K-token step), 32 q / 8 kv heads x 128, bf16."""
