@@ -260,3 +260,32 @@ def test_long_prefix_crosses_table_windows(b, dtype):
     err = row_rel_err(got, ref)
     announce(f"b={b} {dtype} long prefix: max row rel err {err:.3e}")
     assert err <= 2e-3
+
+
+def _random_config(seed):
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f16", "fp8", "f32"][seed % 4]
+    D = [64, 128][(seed // 4) % 2]
+    b = [8, 16, 32][seed % 3]
+    Hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    S = int(rng.integers(1, 5))
+    pre = [int(x) for x in rng.integers(0, 500, S)]
+    chunk = [int(x) for x in rng.integers(0, 160, S)]
+    return W.chunked(f"prand{seed}", 2000 + seed, dtype, pre, chunk, G * Hkv, Hkv, D, block_size=b)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configs(seed):
+    """Randomized shapes across every pool dtype, head dim, block size and
+    group: prefixes 0..499, chunks 0..159 (empty ones included)."""
+    w = _random_config(seed)
+    if sum(w.chunk_lens) == 0:
+        pytest.skip("every chunk empty")
+    got, _, _ = _run(w)
+    ref = OracleRun(w).prefill()
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    announce(f"{w.name} {w.dtype} b={w.block_size} {w.num_q_heads}/{w.num_kv_heads}x{w.head_dim}: "
+             f"max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
