@@ -647,8 +647,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   }
 }
 
+// fp32 pools: each wavefront walks on its own, one sub-tile per step with a
+// second buffer one step ahead, through cached buffer loads.
 template <class Tag, int D, int NQ, class OutT>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
+  static_assert(!Is16<Tag>::value, "16-bit and FP8 pools run prefill_ring_kernel");
   constexpr int ES = Elt<Tag>::bytes;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -699,13 +702,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     const int64_t qrow = has[q] ? ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) : 0;
     qf[q].load(a.q + qrow * D * In<Tag>::bytes, has[q], lane);
   }
-  // FP8: the head's K scale folds into the score scale, its V scale into the output.
-  float qk_scale = a.qk_scale;
-  float v_scale = 1.f;
-  if constexpr (Elt<Tag>::bytes == 1) {
-    qk_scale *= a.k_scales[g];
-    v_scale = a.v_scales[g];
-  }
+  const float qk_scale = a.qk_scale;
 
   // Keys 0 .. p_last, where p_last is the position of the wavefront's last row.
   const int p_last = L - n + row_end - 1;
@@ -752,14 +749,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     f.template load<kPolicyCached>(tile_rsrc(a.k_pool + off, bytes),
                                    tile_rsrc(a.v_pool + off, bytes), lane, a.rows);
   };
-  using CT = typename ComputeTag<Tag>::type;
   auto attend = [&](const Frag<Tag, D>& f, int nv, int i) {
     if (nv <= 0) return;
     const int key0 = (c0 + i) * a.rows;
-    const Frag<CT, D> w = compute_regs(f);
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
-      attend_block<CT, D>(w, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
+      attend_block<Tag, D>(f, qf[q], st[q], nv, qk_scale, lane, pos[q] - key0 + 1);
   };
   for (; c0 < cnt; c0 += kWave) {
     open_table();
@@ -779,7 +774,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     const float l_tot = xor_sum(st[q].l);
     const int t = row0 + q * a.tpg + cr;
     if (!(col_ok && t < row_end)) continue;
-    const float inv = (has[q] && l_tot > 0.f) ? v_scale / l_tot : 0.f;
+    const float inv = (has[q] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
     OutT* o = reinterpret_cast<OutT*>(a.out) +
               ((int64_t)(qs + t) * a.num_q_heads + head0 + chh) * D;
 #pragma unroll
