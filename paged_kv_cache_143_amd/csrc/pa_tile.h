@@ -261,21 +261,13 @@ constexpr float kRescaleLog2 = 8.f;
 // n_valid: stored tokens in the sub-tile (rows past it may hold anything).
 // A column may see none of the sub-tile's rows while its state is still
 // empty (m = -inf, e.g. under a causal limit); its exponent base then falls
-// back to 0 so that -inf - -inf never occurs.
-template <class Tag, int D>
-__device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& qf, State<D>& st,
-                                    int n_valid, float qk_scale, int lane, int lim = kRows) {
-  // 1) scores S[t][h]: lane (h + 16q) gets tokens 4q..4q+3 of head h.
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (Is16<Tag>::value) {
-#pragma unroll
-    for (int m = 0; m < D / 32; ++m) s = mma32<Tag>(f.k[m], qf.q[m], s);
-  } else {
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = mma4(f.k[j][e], qf.q[j][e], s);
-  }
+// back to 0 so that -inf - -inf never occurs.  `qk()` returns the scores,
+// lane (h + 16q) holding tokens 4q..4q+3 of head h; `pv(p, t0)` adds
+// V^T P for this lane's four probabilities p of tokens t0 .. t0 + 3.
+template <int D, class QK, class PV>
+__device__ inline void attend_core(QK qk, PV pv, State<D>& st, int n_valid, float qk_scale,
+                                   int lane, int lim) {
+  f32x4 s = qk();
   const int t0 = 4 * (lane >> 4);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -284,7 +276,7 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
     // column's last visible row + 1) is the causal limit of multi-token queries.
     if (t0 + r >= n_valid || t0 + r >= lim) s[r] = -INFINITY;
   }
-  // 2) online softmax with a lazily moved base: only when some score of the
+  // Online softmax with a lazily moved base: only when some score of the
   // wavefront exceeds its column's base by more than kRescaleLog2 (always on
   // the first sub-tile, where m = -inf) does the wavefront take the column
   // maxima across lanes and rescale l and acc -- a uniform branch; otherwise
@@ -307,8 +299,24 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s[r] - base);
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  // 3) acc[d][h] += V^T P.
-  if constexpr (Is16<Tag>::value) {
+  pv(p, t0);
+}
+
+// The 16-bit matrix-core step over K chunks and V dim tiles read through
+// `kf(m)` and `vf(n)` (registers, or FP8 codes widened at the point of use).
+// acc[d][h] += V^T P with P split into a high and a low part placed in the two
+// k halves against a duplicated V fragment.  Tail tokens of V are zeroed
+// (their P is zero, but 0 * NaN is NaN).
+template <class Tag, int D, class KF, class VF>
+__device__ inline void attend16(KF kf, VF vf, const QFrag<Tag, D>& qf, State<D>& st, int n_valid,
+                                float qk_scale, int lane, int lim = kRows) {
+  auto qk = [&]() {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) s = mma32<Tag>(kf(m), qf.q[m], s);
+    return s;
+  };
+  auto pv = [&](const float* p, int t0) {
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -317,7 +325,6 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
     }
     const u32x4 pb = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
                       lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-    // Tail tokens of V are zeroed (their P is zero, but 0 * NaN is NaN).
     uint32_t keep0 = 0xffffffffu, keep1 = 0xffffffffu;
     if (n_valid < kRows) {
       keep0 = (t0 + 0 < n_valid ? 0x0000ffffu : 0u) | (t0 + 1 < n_valid ? 0xffff0000u : 0u);
@@ -325,22 +332,60 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
     }
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
-      const uint32_t a0 = f.v[n][0] & keep0, a1 = f.v[n][1] & keep1;
+      const u32x2 v = vf(n);
+      const uint32_t a0 = v[0] & keep0, a1 = v[1] & keep1;
       const u32x4 va = {a0, a1, a0, a1};
       st.acc[n] = mma32<Tag>(va, pb, st.acc[n]);
     }
+  };
+  attend_core<D>(qk, pv, st, n_valid, qk_scale, lane, lim);
+}
+
+template <class Tag, int D>
+__device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& qf, State<D>& st,
+                                    int n_valid, float qk_scale, int lane, int lim = kRows) {
+  if constexpr (Is16<Tag>::value) {
+    attend16<Tag, D>([&](int m) { return f.k[m]; }, [&](int n) { return f.v[n]; }, qf, st,
+                     n_valid, qk_scale, lane, lim);
   } else {
+    // fp32: v_mfma_f32_16x16x4_f32, one k per lane.
+    auto qk = [&]() {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
-      f32x4 va = f.v[n];
-      if (n_valid < kRows) {
+      for (int j = 0; j < D / 16; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) va[e] = (t0 + e < n_valid) ? va[e] : 0.f;
+        for (int e = 0; e < 4; ++e) s = mma4(f.k[j][e], qf.q[j][e], s);
+      return s;
+    };
+    auto pv = [&](const float* p, int t0) {
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n) {
+        f32x4 va = f.v[n];
+        if (n_valid < kRows) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) va[e] = (t0 + e < n_valid) ? va[e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.acc[n] = mma4(va[e], p[e], st.acc[n]);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st.acc[n] = mma4(va[e], p[e], st.acc[n]);
-    }
+    };
+    attend_core<D>(qk, pv, st, n_valid, qk_scale, lane, lim);
   }
+}
+
+// FP8 codes: the same step with each K chunk and V dim tile widened to bf16
+// just before its matrix product, so only that chunk's widened registers are
+// live (the raw codes are half the registers of the widened fragment).
+template <int D>
+__device__ inline void attend_block_fp8(const Frag<TagFP8, D>& f, const QFrag<TagFP8, D>& qf,
+                                        State<D>& st, int n_valid, float qk_scale, int lane) {
+  attend16<TagBF16, D>(
+      [&](int m) {
+        return u32x4{fp8x2_to_bf16x2<false>(f.k[m][0]), fp8x2_to_bf16x2<true>(f.k[m][0]),
+                     fp8x2_to_bf16x2<false>(f.k[m][1]), fp8x2_to_bf16x2<true>(f.k[m][1])};
+      },
+      [&](int n) { return u32x2{fp8x2_to_bf16x2<false>(f.v[n]), fp8x2_to_bf16x2<true>(f.v[n])}; },
+      qf, st, n_valid, qk_scale, lane);
 }
 
 // Output dimension of accumulator element acc[n][i] (the MFMA C layout puts
