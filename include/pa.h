@@ -214,11 +214,17 @@ PA_API pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_
  *                     kernel that rescales each partition's (max, sum,
  *                     weighted sum) to the global max; PA_PARTITION_AUTO:
  *                     0 when num_seqs * Hkv already covers the GPU's
- *                     resident workgroups (3 per compute unit of the current
- *                     device), else about 1.75 times that many units, partitions
- *                     of >= 512 tokens rounded to 256 (pa_decode_workspace_size
- *                     with the same arguments on the same device gives the
- *                     matching workspace)
+ *                     resident workgroups (per compute unit of the current
+ *                     device: 3, FP8 pools 4, fp32 pools with head_dim 128 2)
+ *                     or max_context_len <= 512; else the split is planned on
+ *                     the device from the lengths: a sequence of n 16-token
+ *                     tiles (8-token for 8-token blocks of FP8 and fp32
+ *                     pools) is split into ceil(n / u) near-equal ranges, u
+ *                     the smallest tile count of at least 512 tokens for which
+ *                     each KV head's ranges number at most resident / Hkv --
+ *                     one round of near-equal work units
+ *                     (pa_decode_workspace_size with the same arguments on the
+ *                     same device gives the matching workspace)
  *   workspace         device, >= pa_decode_workspace_size bytes (may be NULL
  *                     when that size is 0)
  * Accumulation is fp32 in every dtype; q.k products of f16/bf16 inputs are

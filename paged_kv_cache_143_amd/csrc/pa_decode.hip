@@ -77,8 +77,12 @@ struct DecodeArgs {
   int32_t max_blocks;  // table row width
   int32_t max_len;     // clip for lengths
   int32_t ps;          // partition size in tokens (a multiple of the block size)
-  int32_t num_parts;   // P = ceil(max_len / ps)
+  int32_t num_parts;   // P = ceil(max_len / ps); planned split: units per KV head
   int32_t longest_first;  // 1: map workgroups to sequences in decreasing length
+  int32_t planned;     // 1: split planned from the lengths (automatic partitioning)
+  int32_t part_rows;   // planned split: tokens per tile (16 when 8-token blocks pair up)
+  int32_t min_tiles;   // planned split: smallest unit worth its start-up, in tiles
+  int32_t* plan_hdr;   // planned split: per sequence {record index of unit 0, units}
   float qk_scale;      // scale * log2(e)
   const float* k_scales;  // FP8 pools: per-KV-head scales, else null
   const float* v_scales;
@@ -103,12 +107,18 @@ constexpr int kPairwiseRankMax = PA_PAIRWISE_RANK_MAX;
 
 
 
-__device__ inline int rank_bin(const DecodeArgs& a, int i) {
+// Length of sequence i as attended: clipped to [0, max_len] and to what its
+// table row can address.
+__device__ inline int clip_len(const DecodeArgs& a, int i) {
   int L = a.lens[i];
   L = L < 0 ? 0 : L;
   L = L > a.max_len ? a.max_len : L;
   const int64_t cap = (int64_t)a.max_blocks * a.block_size;
-  if ((int64_t)L > cap) L = (int)cap;
+  return (int64_t)L > cap ? (int)cap : L;
+}
+
+__device__ inline int rank_bin(const DecodeArgs& a, int i) {
+  const int L = clip_len(a, i);
   int nb = (L + kRows - 1) / kRows;          // work measure: 16-token sub-tiles
   nb = nb > kRankBins - 1 ? kRankBins - 1 : nb;
   return kRankBins - 1 - nb;                   // longest first
@@ -204,6 +214,96 @@ __device__ inline int seq_of_rank_pairwise(const DecodeArgs& a, int r, int* lds)
   __syncthreads();
   return seq;
 }
+
+// ---- planned split (automatic partitioning) ----
+// When the (sequence, KV head) pairs are fewer than the resident workgroups,
+// each sequence's tiles are split into units sized from the lengths: a
+// sequence of n tiles gets ceil(n / u) units (one if it is empty), each a
+// near-equal range of its tiles, where u is the smallest tile count of at
+// least min_tiles for which one KV head's units number at most num_parts.
+// This divisor rule gives the smallest largest unit for that many units, so
+// the grid is one round of units of nearly equal work.  Every wavefront of
+// the partition kernel derives the same plan from the lengths; the unit that
+// starts a sequence's first KV head leaves the sequence's (first record,
+// units) in a header for the combine kernel.  Reductions are DPP sums.
+__device__ inline int plan_tiles(const DecodeArgs& a, int i) {
+  return (clip_len(a, i) + a.part_rows - 1) / a.part_rows;
+}
+
+// Units of a sequence of n tiles under unit size u, capped at num_parts + 1
+// (only comparisons with num_parts are made; the cap keeps sums in range).
+__device__ inline int plan_units(const DecodeArgs& a, int n, int u) {
+  const int c = n <= u ? 1 : (n - 1) / u + 1;
+  return c > a.num_parts ? a.num_parts + 1 : c;
+}
+
+// One KV head's units under unit size u (n0: the tiles of sequence `lane`).
+__device__ inline int plan_count(const DecodeArgs& a, int n0, int u, int lane) {
+  int c = lane < a.num_seqs ? plan_units(a, n0, u) : 0;
+  for (int i = kWave + lane; i < a.num_seqs; i += kWave) c += plan_units(a, plan_tiles(a, i), u);
+  return __reduce_add_sync(~0ull, c);
+}
+
+// Unit size u of the plan.  n0 receives the tile count of sequence `lane`
+// (the first 64 sequences stay in a register across the search).
+__device__ inline int plan_unit_size(const DecodeArgs& a, int lane, int& n0) {
+  const int S = a.num_seqs;
+  n0 = lane < S ? plan_tiles(a, lane) : 0;
+  // The total in 16-bit halves: each half's 32-bit sum cannot overflow.
+  int lo16 = n0 & 0xffff, hi16 = n0 >> 16, mx = n0;
+  for (int i = kWave + lane; i < S; i += kWave) {
+    const int n = plan_tiles(a, i);
+    lo16 += n & 0xffff;
+    hi16 += n >> 16;
+    mx = max(mx, n);
+  }
+  const int64_t tot = (int64_t)__reduce_add_sync(~0ull, hi16) * 65536 + __reduce_add_sync(~0ull, lo16);
+  mx = __reduce_max_sync(~0ull, mx);
+  int lo = (int)((tot + a.num_parts - 1) / a.num_parts);
+  lo = max(lo, a.min_tiles);
+  int hi = max(lo, mx);
+  if (hi > lo && plan_count(a, n0, lo, lane) <= a.num_parts) hi = lo;   // the floor fits
+  while (lo < hi) {                            // smallest u with count(u) <= num_parts
+    const int mid = lo + ((hi - lo) >> 1);
+    if (plan_count(a, n0, mid, lane) <= a.num_parts) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+struct PlanUnit {
+  int seq;     // -1: past the plan's last unit
+  int part;    // unit index within the sequence
+  int count;   // units of the sequence
+  int first;   // record index of the sequence's unit 0 among its KV head's records
+};
+
+// Unit r of one KV head: units are numbered sequence by sequence.
+__device__ inline PlanUnit plan_locate(const DecodeArgs& a, int n0, int u, int r, int lane) {
+  const int S = a.num_seqs;
+  int base = 0;
+  for (int c = 0; c < S; c += kWave) {
+    const int i = c + lane;
+    const int n = c == 0 ? n0 : (i < S ? plan_tiles(a, i) : 0);
+    const int np = i < S ? plan_units(a, n, u) : 0;
+    int incl = np;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const unsigned long long hit = __ballot(base + incl > r);
+    if (hit) {
+      // Lane values, made scalar: they stay live to the end of the kernel.
+      const int l = __builtin_ctzll(hit);
+      const int excl = __builtin_amdgcn_readlane(incl - np, l);
+      return {c + l, r - base - excl, __builtin_amdgcn_readlane(np, l), base + excl};
+    }
+    base += __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  return {-1, 0, 0, 0};
+}
+
 
 // The fused step writes the current token (offset o of its block) to the pool
 // and, for the one block that holds it, replaces the loaded values of that
@@ -468,18 +568,28 @@ void decode_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int g = unit % a.num_kv_heads;
   const int rest = unit / a.num_kv_heads;
-  const int part = rest / a.num_seqs;
-  const int seq = !a.longest_first ? rest % a.num_seqs
+  PlanUnit pu{0, 0, 0, 0};
+  if (a.planned) {
+    int n0;
+    const int u = plan_unit_size(a, lane, n0);
+    pu = plan_locate(a, n0, u, rest, lane);
+    if (pu.seq < 0) return;                      // the grid's spare units
+  }
+  // The combine kernel's header of a planned sequence, stored where few
+  // registers are live (at exit).
+  auto put_header = [&]() {
+    if (a.planned && g == 0 && pu.part == 0 && threadIdx.x == 0)
+      *reinterpret_cast<int2*>(a.plan_hdr + 2 * pu.seq) = make_int2(pu.first, pu.count);
+  };
+  const int part = a.planned ? pu.part : rest / a.num_seqs;
+  const int seq = a.planned ? pu.seq
+                  : !a.longest_first ? rest % a.num_seqs
                   : a.num_seqs <= kPairwiseRankMax
                       ? seq_of_rank_pairwise(a, rest % a.num_seqs, reinterpret_cast<int*>(smem))
                       : seq_of_rank(a, rest % a.num_seqs, reinterpret_cast<int*>(smem));
 
-  int L = a.lens[seq];
-  L = L < 0 ? 0 : L;
-  L = L > a.max_len ? a.max_len : L;
-  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
-  if ((int64_t)L > cap) L = (int)cap;
-  const int n_parts = (L + a.ps - 1) / a.ps;
+  const int L = clip_len(a, seq);
+  const int n_parts = a.planned ? pu.count : (L + a.ps - 1) / a.ps;
   const int G = a.group;
   const int head0 = g * G;
 
@@ -488,6 +598,7 @@ void decode_kernel(DecodeArgs a) {
       OutT* o = reinterpret_cast<OutT*>(a.out) + ((int64_t)seq * a.num_q_heads + head0) * D;
       for (int i = threadIdx.x; i < G * D; i += kThreads) store_out<OutT>(o + i, 0.f);
     }
+    put_header();
     return;
   }
   if (part >= n_parts) return;
@@ -496,8 +607,9 @@ void decode_kernel(DecodeArgs a) {
   // 8-token blocks when P8).
   const int rows = P8 ? kRows : a.rows;
   const int nsub_seq = (L + rows - 1) / rows;
-  const int j0 = part * (a.ps / rows);
-  const int j1 = min(nsub_seq, j0 + a.ps / rows);
+  const int j0 = a.planned ? (int)((int64_t)part * nsub_seq / n_parts) : part * (a.ps / rows);
+  const int j1 = a.planned ? (int)((int64_t)(part + 1) * nsub_seq / n_parts)
+                           : min(nsub_seq, j0 + a.ps / rows);
   const int per = (j1 - j0 + kWaves - 1) / kWaves;  // tiles per wavefront: contiguous quarters
   const int first = min(j1, j0 + wave * per);
   const int cnt = max(0, min(j1, first + per) - first);
@@ -679,6 +791,7 @@ void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
+  put_header();
   const bool single = n_parts == 1;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int hh = idx / D;
@@ -701,7 +814,9 @@ void decode_kernel(DecodeArgs a) {
       store_out<OutT>(reinterpret_cast<OutT*>(a.out) + row * D + d, val);
     } else {
       // One contiguous record per unit: its writes touch the fewest lines.
-      float* rec = a.part + (((int64_t)seq * a.num_kv_heads + g) * a.num_parts + part) * a.part_stride;
+      const int64_t r = a.planned ? (int64_t)g * a.num_parts + pu.first + part
+                                  : ((int64_t)seq * a.num_kv_heads + g) * a.num_parts + part;
+      float* rec = a.part + r * a.part_stride;
       rec[hh * D + d] = val;
       if (d == 0) {
         rec[G * D + hh] = M;
@@ -720,17 +835,21 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   const int64_t row = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
   if (row >= (int64_t)a.num_seqs * a.num_q_heads) return;
   const int seq = (int)(row / a.num_q_heads);
-  int L = a.lens[seq];
-  L = L < 0 ? 0 : L;
-  L = L > a.max_len ? a.max_len : L;
-  const int64_t cap = (int64_t)a.max_blocks * a.block_size;
-  if ((int64_t)L > cap) L = (int)cap;
-  const int n_parts = (L + a.ps - 1) / a.ps;
+  int n_parts, first = 0;
+  if (a.planned) {
+    const int2 hd = *reinterpret_cast<const int2*>(a.plan_hdr + 2 * seq);
+    first = hd.x;
+    n_parts = first >= 0 && hd.y <= a.num_parts - first ? hd.y : 0;   // in the records
+  } else {
+    n_parts = (clip_len(a, seq) + a.ps - 1) / a.ps;
+  }
   if (n_parts <= 1) return;
   const int h = (int)(row - (int64_t)seq * a.num_q_heads);
   const int G = a.group;
   const int g = h / G, hh = h - g * G;
-  const float* rec0 = a.part + ((int64_t)seq * a.num_kv_heads + g) * a.num_parts * a.part_stride;
+  const int64_t rec_first = a.planned ? (int64_t)g * a.num_parts + first
+                                      : ((int64_t)seq * a.num_kv_heads + g) * a.num_parts;
+  const float* rec0 = a.part + rec_first * a.part_stride;
   const float* pm = rec0 + G * D + hh;            // m of partition p at pm[p * stride]
   const float* pl = pm + G;
   const int64_t stride = a.part_stride;
@@ -759,7 +878,7 @@ template <class Tag, int D, class OutT, bool P8>
 static pa_status launch(const DecodeArgs& a, int64_t units, size_t lds, hipStream_t stream) {
   decode_kernel<Tag, D, OutT, P8><<<(unsigned)units, kThreads, lds, stream>>>(a);
   pa_status st = launch_status();
-  if (st != PA_OK || a.num_parts <= 1) return st;
+  if (st != PA_OK || (a.num_parts <= 1 && !a.planned)) return st;
   const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
   reduce_kernel<D, OutT><<<(unsigned)((rows + kWaves - 1) / kWaves), kThreads, 0, stream>>>(a);
   return launch_status();
@@ -781,31 +900,47 @@ static pa_status dispatch_16(bool p8, int D, const DecodeArgs& a, int64_t units,
 
 // Partition geometry shared by the size query and the launch.
 // Automatic partitioning: one unit per (sequence, KV head) already fills the
-// GPU when there are at least as many units as resident workgroups (3 per
-// compute unit); otherwise split so there are about 1.75 times that many, in
-// partitions of at least 512 tokens, a multiple of 256 (short units lose more
-// to their start-up latency than they gain in balance; measured on the
-// 16 x 8K..32K-token workload, 3072-token partitions).
-static int32_t auto_partition(int64_t base_units, int32_t max_len) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * 3;
-  if (base_units >= slots || max_len <= 512) return 0;
-  const int64_t parts = (7 * slots + 4 * base_units - 1) / (4 * base_units);
-  int64_t ps = (max_len + parts - 1) / parts;
-  ps = (ps + 255) / 256 * 256;
-  return (int32_t)std::max<int64_t>(ps, 512);
+// GPU when there are at least as many units as resident workgroups (one per
+// wavefront slot of a SIMD on every compute unit); otherwise the split is
+// planned from the lengths in the kernels (one round of near-equal units,
+// num_parts of them per KV head), unless no sequence can be longer than the
+// smallest unit worth splitting off.
+constexpr int32_t kMinPlannedTokens = 512;
+
+static int32_t resident_per_cu(pa_dtype dt, int32_t D) {
+  if (dt == PA_F32 && D == 128) return 2;
+  return dt == PA_FP8_E4M3 ? PA_FP8_WAVES_PER_EU : PA_WAVES_PER_EU;
 }
 
-static void geometry(int32_t max_len, int32_t partition_size, int64_t base_units, int32_t b,
-                     int32_t* ps, int32_t* parts) {
-  if (partition_size == PA_PARTITION_AUTO) partition_size = auto_partition(base_units, max_len);
+struct Geometry {
+  int32_t ps;        // partition size in tokens (fixed partitions)
+  int32_t parts;     // partitions per sequence, or units per KV head when planned
+  bool planned;
+};
+
+static Geometry geometry(const pa_pool_desc* pool, int32_t num_seqs, int32_t max_len,
+                         int32_t partition_size) {
+  Geometry geo{0, 1, false};
+  if (partition_size == PA_PARTITION_AUTO) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t slots =
+        (int64_t)(cus > 0 ? cus : 256) * resident_per_cu(pool->dtype, pool->head_dim);
+    if ((int64_t)num_seqs * pool->num_kv_heads < slots && max_len > kMinPlannedTokens) {
+      geo.planned = true;
+      geo.parts = (int32_t)(slots / pool->num_kv_heads);
+      return geo;
+    }
+    partition_size = 0;
+  }
   // One partition: whole 16-token tiles (8-token blocks then walk in pairs).
+  const int32_t b = pool->block_size;
   const int32_t unit = b < 16 ? 16 : b;
   const int32_t whole = ((max_len > 0 ? max_len : 1) + unit - 1) / unit * unit;
-  *ps = partition_size == 0 ? whole : partition_size;
-  *parts = max_len > 0 ? (max_len + *ps - 1) / *ps : 1;
+  geo.ps = partition_size == 0 ? whole : partition_size;
+  geo.parts = max_len > 0 ? (max_len + geo.ps - 1) / geo.ps : 1;
+  return geo;
 }
 
 static bool partition_ok(int32_t partition_size, int32_t b) {
@@ -816,9 +951,21 @@ static bool partition_ok(int32_t partition_size, int32_t b) {
 // to whole 128-byte lines.
 static int32_t record_floats(int32_t G, int32_t D) { return (G * D + 2 * G + 31) / 32 * 32; }
 
-static size_t workspace_bytes(int64_t units_per_part, int32_t parts, int32_t G, int32_t D) {
-  if (parts <= 1) return 0;
-  return (size_t)(units_per_part * parts * (int64_t)record_floats(G, D) * 4);
+// Records: one per (KV head, unit) when planned, else per (sequence, KV head,
+// partition); none without a split.
+static size_t record_bytes(const Geometry& geo, int32_t num_seqs, int32_t Hkv, int32_t G,
+                           int32_t D) {
+  int64_t records;
+  if (geo.planned) records = (int64_t)Hkv * geo.parts;
+  else if (geo.parts > 1) records = (int64_t)num_seqs * Hkv * geo.parts;
+  else return 0;
+  return (size_t)(records * (int64_t)record_floats(G, D) * 4);
+}
+
+// The records, then (planned split) two ints per sequence.
+static size_t workspace_bytes(const Geometry& geo, int32_t num_seqs, int32_t Hkv, int32_t G,
+                              int32_t D) {
+  return record_bytes(geo, num_seqs, Hkv, G, D) + (geo.planned ? (size_t)num_seqs * 8 : 0);
 }
 
 
@@ -852,14 +999,11 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(q)) return PA_ERR_INVALID_ARG;
   if (!(scale == scale)) return PA_ERR_INVALID_ARG;
 
-  int32_t ps, parts;
-  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads,
-           pool->block_size, &ps, &parts);
-  const size_t need = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts, G,
-                                      pool->head_dim);
+  const Geometry geo = geometry(pool, num_seqs, max_context_len, partition_size);
+  const size_t need = workspace_bytes(geo, num_seqs, pool->num_kv_heads, G, pool->head_dim);
   if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
-  const int64_t units = (int64_t)pool->num_kv_heads * num_seqs * parts;
+  const int64_t units = (int64_t)pool->num_kv_heads * (geo.planned ? 1 : num_seqs) * geo.parts;
   if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
 
   DecodeArgs a;
@@ -873,6 +1017,10 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   a.tables = block_tables;
   a.lens = context_lens;
   a.part = need > 0 ? (float*)workspace : nullptr;
+  a.plan_hdr = geo.planned ? (int32_t*)((char*)workspace +
+                                        record_bytes(geo, num_seqs, pool->num_kv_heads, G,
+                                                     pool->head_dim))
+                           : nullptr;
   a.part_stride = record_floats(G, pool->head_dim);
   a.num_blocks = pool->num_blocks;
   a.block_size = pool->block_size;
@@ -884,12 +1032,13 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.max_len = max_context_len;
-  a.ps = ps;
-  a.num_parts = parts;
+  a.ps = geo.ps;
+  a.num_parts = geo.parts;
+  a.planned = geo.planned;
 #ifdef PA_NO_LONGEST_FIRST
   a.longest_first = 0;
 #else
-  a.longest_first = 1;
+  a.longest_first = !geo.planned;                // planned units are of near-equal work
 #endif
   a.qk_scale = scale * kLog2e;
   a.k_scales = pool->k_scales;
@@ -901,7 +1050,9 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   if (a.longest_first) lds = std::max(lds, (size_t)kRankLdsInts * sizeof(int));
   const hipStream_t s = (hipStream_t)stream;
   const int D = pool->head_dim;
-  const bool p8 = pool->block_size == 8 && ps % 16 == 0;
+  const bool p8 = pool->block_size == 8 && (geo.planned || geo.ps % 16 == 0);
+  a.part_rows = p8 && (pool->dtype == PA_BF16 || pool->dtype == PA_F16) ? 16 : a.rows;
+  a.min_tiles = kMinPlannedTokens / a.part_rows;
 
   switch (pool->dtype) {
     case PA_BF16:
@@ -935,11 +1086,9 @@ pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
       !partition_ok(partition_size, pool->block_size))
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads) return PA_ERR_INVALID_ARG;
-  int32_t ps, parts;
-  geometry(max_context_len, partition_size, (int64_t)num_seqs * pool->num_kv_heads,
-           pool->block_size, &ps, &parts);
-  *bytes = workspace_bytes((int64_t)num_seqs * pool->num_kv_heads, parts,
-                           num_q_heads / pool->num_kv_heads, pool->head_dim);
+  const Geometry geo = geometry(pool, num_seqs, max_context_len, partition_size);
+  *bytes = workspace_bytes(geo, num_seqs, pool->num_kv_heads, num_q_heads / pool->num_kv_heads,
+                           pool->head_dim);
   return PA_OK;
 }
 

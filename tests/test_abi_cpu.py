@@ -57,8 +57,15 @@ def test_workspace_size_host_only():
     st, n = B.pa_decode_workspace_size(d, 256, 32, 2000, auto)
     assert st == B.PA_OK and n == 0                # 2048 units already cover 768 slots
     st, n = B.pa_decode_workspace_size(d, 16, 64, 32768, auto)
-    parts = -(-32768 // 3072)                      # 11 parts wanted -> 2979 -> 3072 tokens
-    assert st == B.PA_OK and n == 16 * 8 * parts * rec * 4
+    # 128 units < 768 slots: a planned split, one record per (KV head, slot share),
+    # then two ints per sequence
+    assert st == B.PA_OK and n == 8 * (768 // 8) * rec * 4 + 16 * 8
+    d8 = _desc(dtype="fp8")
+    d8.k_scales = d8.v_scales = 256                # never read by the size query
+    st, n = B.pa_decode_workspace_size(d8, 16, 64, 32768, auto)
+    assert st == B.PA_OK and n == 8 * (1024 // 8) * rec * 4 + 16 * 8   # FP8: 4 waves per SIMD
+    st, n = B.pa_decode_workspace_size(d, 16, 64, 512, auto)
+    assert st == B.PA_OK and n == 0                # nothing longer than one 512-token unit
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, -2)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, 500)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(_desc(head_dim=96), 1, 8, 16, 0)[0] == B.PA_ERR_UNSUPPORTED
