@@ -80,7 +80,7 @@ struct DecodeArgs {
   int32_t num_parts;   // P = ceil(max_len / ps); planned split: units per KV head
   int32_t longest_first;  // 1: map workgroups to sequences in decreasing length
   int32_t planned;     // 1: split planned from the lengths (automatic partitioning)
-  int32_t part_rows;   // planned split: tokens per tile (16 when 8-token blocks pair up)
+  int32_t part_shift;  // planned split: log2 of tokens per tile (16 when 8-token blocks pair up)
   int32_t min_tiles;   // planned split: smallest unit worth its start-up, in tiles
   int32_t* plan_hdr;   // planned split: per sequence {record index of unit 0, units}
   float qk_scale;      // scale * log2(e)
@@ -226,9 +226,10 @@ __device__ inline int seq_of_rank_pairwise(const DecodeArgs& a, int r, int* lds)
 // the partition kernel derives the same plan from the lengths; the unit that
 // starts a sequence's first KV head leaves the sequence's (first record,
 // units) in a header for the combine kernel.  Reductions are DPP sums.
-__device__ inline int plan_tiles(const DecodeArgs& a, int i) {
-  return (clip_len(a, i) + a.part_rows - 1) / a.part_rows;
+__device__ inline int plan_tiles_of(const DecodeArgs& a, int L) {
+  return (L + (1 << a.part_shift) - 1) >> a.part_shift;
 }
+__device__ inline int plan_tiles(const DecodeArgs& a, int i) { return plan_tiles_of(a, clip_len(a, i)); }
 
 // Units of a sequence of n tiles under unit size u, capped at num_parts + 1
 // (only comparisons with num_parts are made; the cap keeps sums in range).
@@ -244,11 +245,12 @@ __device__ inline int plan_count(const DecodeArgs& a, int n0, int u, int lane) {
   return __reduce_add_sync(~0ull, c);
 }
 
-// Unit size u of the plan.  n0 receives the tile count of sequence `lane`
-// (the first 64 sequences stay in a register across the search).
-__device__ inline int plan_unit_size(const DecodeArgs& a, int lane, int& n0) {
+// Unit size u of the plan.  L0 receives the length of sequence `lane` (the
+// first 64 sequences stay in registers across the search).
+__device__ inline int plan_unit_size(const DecodeArgs& a, int lane, int& L0) {
   const int S = a.num_seqs;
-  n0 = lane < S ? plan_tiles(a, lane) : 0;
+  L0 = lane < S ? clip_len(a, lane) : 0;
+  const int n0 = plan_tiles_of(a, L0);
   // The total in 16-bit halves: each half's 32-bit sum cannot overflow.
   int lo16 = n0 & 0xffff, hi16 = n0 >> 16, mx = n0;
   for (int i = kWave + lane; i < S; i += kWave) {
@@ -257,9 +259,15 @@ __device__ inline int plan_unit_size(const DecodeArgs& a, int lane, int& n0) {
     hi16 += n >> 16;
     mx = max(mx, n);
   }
-  const int64_t tot = (int64_t)__reduce_add_sync(~0ull, hi16) * 65536 + __reduce_add_sync(~0ull, lo16);
+  const int tot_hi = __reduce_add_sync(~0ull, hi16), tot_lo = __reduce_add_sync(~0ull, lo16);
   mx = __reduce_max_sync(~0ull, mx);
-  int lo = (int)((tot + a.num_parts - 1) / a.num_parts);
+  int lo;
+  if (tot_hi < 0x7c00) {                       // the total fits 31 bits: 32-bit division
+    lo = (int)(((unsigned)tot_hi << 16) + (unsigned)tot_lo);
+    lo = (int)(((unsigned)lo + a.num_parts - 1) / (unsigned)a.num_parts);
+  } else {
+    lo = (int)(((int64_t)tot_hi * 65536 + tot_lo + a.num_parts - 1) / a.num_parts);
+  }
   lo = max(lo, a.min_tiles);
   int hi = max(lo, mx);
   if (hi > lo && plan_count(a, n0, lo, lane) <= a.num_parts) hi = lo;   // the floor fits
@@ -276,16 +284,17 @@ struct PlanUnit {
   int part;    // unit index within the sequence
   int count;   // units of the sequence
   int first;   // record index of the sequence's unit 0 among its KV head's records
+  int len;     // the sequence's clipped length
 };
 
 // Unit r of one KV head: units are numbered sequence by sequence.
-__device__ inline PlanUnit plan_locate(const DecodeArgs& a, int n0, int u, int r, int lane) {
+__device__ inline PlanUnit plan_locate(const DecodeArgs& a, int L0, int u, int r, int lane) {
   const int S = a.num_seqs;
   int base = 0;
   for (int c = 0; c < S; c += kWave) {
     const int i = c + lane;
-    const int n = c == 0 ? n0 : (i < S ? plan_tiles(a, i) : 0);
-    const int np = i < S ? plan_units(a, n, u) : 0;
+    const int Li = c == 0 ? L0 : (i < S ? clip_len(a, i) : 0);
+    const int np = i < S ? plan_units(a, plan_tiles_of(a, Li), u) : 0;
     int incl = np;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -297,11 +306,12 @@ __device__ inline PlanUnit plan_locate(const DecodeArgs& a, int n0, int u, int r
       // Lane values, made scalar: they stay live to the end of the kernel.
       const int l = __builtin_ctzll(hit);
       const int excl = __builtin_amdgcn_readlane(incl - np, l);
-      return {c + l, r - base - excl, __builtin_amdgcn_readlane(np, l), base + excl};
+      return {c + l, r - base - excl, __builtin_amdgcn_readlane(np, l), base + excl,
+              __builtin_amdgcn_readlane(Li, l)};
     }
     base += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
-  return {-1, 0, 0, 0};
+  return {-1, 0, 0, 0, 0};
 }
 
 
@@ -568,11 +578,11 @@ void decode_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int g = unit % a.num_kv_heads;
   const int rest = unit / a.num_kv_heads;
-  PlanUnit pu{0, 0, 0, 0};
+  PlanUnit pu{0, 0, 0, 0, 0};
   if (a.planned) {
-    int n0;
-    const int u = plan_unit_size(a, lane, n0);
-    pu = plan_locate(a, n0, u, rest, lane);
+    int L0;
+    const int u = plan_unit_size(a, lane, L0);
+    pu = plan_locate(a, L0, u, rest, lane);
     if (pu.seq < 0) return;                      // the grid's spare units
   }
   // The combine kernel's header of a planned sequence, stored where few
@@ -588,7 +598,7 @@ void decode_kernel(DecodeArgs a) {
                       ? seq_of_rank_pairwise(a, rest % a.num_seqs, reinterpret_cast<int*>(smem))
                       : seq_of_rank(a, rest % a.num_seqs, reinterpret_cast<int*>(smem));
 
-  const int L = clip_len(a, seq);
+  const int L = a.planned ? pu.len : clip_len(a, seq);
   const int n_parts = a.planned ? pu.count : (L + a.ps - 1) / a.ps;
   const int G = a.group;
   const int head0 = g * G;
@@ -827,13 +837,34 @@ void decode_kernel(DecodeArgs a) {
 }
 
 // Combine partitions: out = sum_p c_p l_p o_p / sum_p c_p l_p, c_p = exp2(m_p - max m).
-// One wavefront per (sequence, query head); rows with one partition were
-// already written by the partition kernel.
+// One workgroup per (sequence, query head); rows with one partition were
+// already written by the partition kernel.  The partitions are read in
+// parallel, not one after another: each thread takes one partition's (m, l)
+// (chunks of kThreads), the weights c_p l_p go to LDS, and the G-row slices
+// o_p are summed as float4 quads by kThreads / (D / 4) partition slots at
+// once, then across slots in LDS.  A row then costs about two memory round
+// trips whatever its number of partitions up to kThreads.
+__device__ inline float block_max(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
 template <int D, class OutT>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
-  if (row >= (int64_t)a.num_seqs * a.num_q_heads) return;
+  constexpr int Q = D / 4;                 // float4 quads of one head's row
+  constexpr int kSlots = kThreads / Q;     // partitions summed at once
+  __shared__ float s_w[kThreads];
+  __shared__ f32x4 s_acc[kThreads];
+  __shared__ float s_red[kWaves];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
   const int seq = (int)(row / a.num_q_heads);
   int n_parts, first = 0;
   if (a.planned) {
@@ -850,28 +881,54 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   const int64_t rec_first = a.planned ? (int64_t)g * a.num_parts + first
                                       : ((int64_t)seq * a.num_kv_heads + g) * a.num_parts;
   const float* rec0 = a.part + rec_first * a.part_stride;
-  const float* pm = rec0 + G * D + hh;            // m of partition p at pm[p * stride]
-  const float* pl = pm + G;
   const int64_t stride = a.part_stride;
-  float M = -INFINITY;
-  for (int p = lane; p < n_parts; p += kWave) M = fmaxf(M, pm[p * stride]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  constexpr int PER = D / kWave;           // dims per lane: 1 or 2
-  float num[PER] = {};
+  const float* pm = rec0 + G * D + hh;             // m of partition p at pm[p * stride]
+  const float* pl = pm + G;
+
+  const float m_own = t < n_parts ? pm[t * stride] : -INFINITY;
+  const float l_own = t < n_parts ? pl[t * stride] : 0.f;
+  float M = m_own;
+  for (int p = t + kThreads; p < n_parts; p += kThreads) M = fmaxf(M, pm[p * stride]);
+  M = block_max(M, s_red);
+
+  const int q = t % Q, slot = t / Q;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (M != -INFINITY) {
-    for (int p = 0; p < n_parts; ++p) {
-      const float w = fast_exp2(pm[p * stride] - M) * pl[p * stride];
+  if (M != -INFINITY) {                            // uniform
+    for (int p0 = 0; p0 < n_parts; p0 += kThreads) {
+      const int p = p0 + t;
+      float w = 0.f;
+      if (p0 == 0) w = fast_exp2(m_own - M) * l_own;
+      else if (p < n_parts) w = fast_exp2(pm[p * stride] - M) * pl[p * stride];
       den += w;
-      const float* op = rec0 + p * stride + hh * D;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += w * op[lane + e * kWave];
+      s_w[t] = w;
+      __syncthreads();
+      const int n = min(kThreads, n_parts - p0);
+      const float* o0 = rec0 + (int64_t)p0 * stride + hh * D + 4 * q;
+#pragma unroll 4
+      for (int i = slot; i < n; i += kSlots) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(o0 + (int64_t)i * stride);
+        const float wi = s_w[i];
+        num += wi * o;
+      }
+      __syncthreads();
     }
   }
-  OutT* o = reinterpret_cast<OutT*>(a.out) + row * D;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) store_out<OutT>(o + lane + e * kWave, den > 0.f ? num[e] / den : 0.f);
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  if ((t & (kWave - 1)) == 0) s_red[t / kWave] = den;
+  s_acc[t] = num;
+  __syncthreads();
+  if (slot == 0) {
+    float dsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) dsum += s_red[w];
+#pragma unroll
+    for (int k = 1; k < kSlots; ++k) num += s_acc[k * Q + q];
+    OutT* out = reinterpret_cast<OutT*>(a.out) + row * D + 4 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out<OutT>(out + e, dsum > 0.f ? num[e] / dsum : 0.f);
+  }
 }
 
 template <class Tag, int D, class OutT, bool P8>
@@ -880,7 +937,7 @@ static pa_status launch(const DecodeArgs& a, int64_t units, size_t lds, hipStrea
   pa_status st = launch_status();
   if (st != PA_OK || (a.num_parts <= 1 && !a.planned)) return st;
   const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
-  reduce_kernel<D, OutT><<<(unsigned)((rows + kWaves - 1) / kWaves), kThreads, 0, stream>>>(a);
+  reduce_kernel<D, OutT><<<(unsigned)rows, kThreads, 0, stream>>>(a);
   return launch_status();
 }
 
@@ -1004,7 +1061,11 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   if (need > 0 && (!workspace || workspace_size < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
   const int64_t units = (int64_t)pool->num_kv_heads * (geo.planned ? 1 : num_seqs) * geo.parts;
-  if (units > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  // A dispatch counts its work-items in 32 bits.
+  constexpr int64_t kMaxGroups = (int64_t)UINT32_MAX / kThreads;
+  if (units > kMaxGroups) return PA_ERR_UNSUPPORTED;
+  if ((geo.planned || geo.parts > 1) && (int64_t)num_seqs * num_q_heads > kMaxGroups)
+    return PA_ERR_UNSUPPORTED;                   // the combine kernel's rows
 
   DecodeArgs a;
   a.k_pool = (char*)k_pool;
@@ -1051,8 +1112,9 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   const hipStream_t s = (hipStream_t)stream;
   const int D = pool->head_dim;
   const bool p8 = pool->block_size == 8 && (geo.planned || geo.ps % 16 == 0);
-  a.part_rows = p8 && (pool->dtype == PA_BF16 || pool->dtype == PA_F16) ? 16 : a.rows;
-  a.min_tiles = kMinPlannedTokens / a.part_rows;
+  const int part_rows = p8 && (pool->dtype == PA_BF16 || pool->dtype == PA_F16) ? 16 : a.rows;
+  a.part_shift = part_rows == 16 ? 4 : 3;      // rows: 8 or 16
+  a.min_tiles = kMinPlannedTokens / part_rows;
 
   switch (pool->dtype) {
     case PA_BF16:
