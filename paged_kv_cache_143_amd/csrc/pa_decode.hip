@@ -837,34 +837,58 @@ void decode_kernel(DecodeArgs a) {
 }
 
 // Combine partitions: out = sum_p c_p l_p o_p / sum_p c_p l_p, c_p = exp2(m_p - max m).
-// One workgroup per (sequence, query head); rows with one partition were
-// already written by the partition kernel.  The partitions are read in
-// parallel, not one after another: each thread takes one partition's (m, l)
-// (chunks of kThreads), the weights c_p l_p go to LDS, and the G-row slices
-// o_p are summed as float4 quads by kThreads / (D / 4) partition slots at
-// once, then across slots in LDS.  A row then costs about two memory round
-// trips whatever its number of partitions up to kThreads.
-__device__ inline float block_max(float x, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = x;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
-  __syncthreads();
-  return r;
+// RT threads per (sequence, query head) row: a whole workgroup when rows are
+// few or partitions many, one wavefront (four rows per workgroup) when rows
+// are many and partitions few.  Rows with one partition were already written
+// by the partition kernel.  The partitions are read in parallel, not one
+// after another: each thread takes one partition's (m, l) (chunks of RT), the
+// weights c_p l_p go to LDS, and the G-row slices o_p are summed as float4
+// quads by RT / (D / 4) partition slots at once, then across slots in LDS.
+// A row then costs about two memory round trips up to RT partitions.
+template <int RT>
+__device__ inline void row_sync() {
+  if constexpr (RT == kWave) {                 // wave-synchronous LDS
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
 }
 
-template <int D, class OutT>
+template <int RT>
+__device__ inline float row_max(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  if constexpr (RT == kWave) {
+    return x;
+  } else {
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = x;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < RT / kWave; ++w) r = fmaxf(r, red[w]);
+    __syncthreads();
+    return r;
+  }
+}
+
+template <int D, class OutT, int RT>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   constexpr int Q = D / 4;                 // float4 quads of one head's row
-  constexpr int kSlots = kThreads / Q;     // partitions summed at once
-  __shared__ float s_w[kThreads];
-  __shared__ f32x4 s_acc[kThreads];
-  __shared__ float s_red[kWaves];
-  const int t = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  constexpr int kSlots = RT / Q;           // partitions summed at once
+  constexpr int kRowsPer = kThreads / RT;
+  constexpr int kWavesPer = RT / kWave;    // wavefronts of one row
+  __shared__ float s_w_all[kThreads];
+  __shared__ f32x4 s_acc_all[kThreads];
+  __shared__ float s_red_all[kWaves];
+  const int t = threadIdx.x % RT;
+  const int sub = threadIdx.x / RT;
+  float* s_w = s_w_all + sub * RT;
+  f32x4* s_acc = s_acc_all + sub * RT;
+  float* s_red = s_red_all + sub * kWavesPer;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPer + sub;
+  if (row >= (int64_t)a.num_seqs * a.num_q_heads) return;     // RT == kWave only
   const int seq = (int)(row / a.num_q_heads);
   int n_parts, first = 0;
   if (a.planned) {
@@ -888,22 +912,22 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   const float m_own = t < n_parts ? pm[t * stride] : -INFINITY;
   const float l_own = t < n_parts ? pl[t * stride] : 0.f;
   float M = m_own;
-  for (int p = t + kThreads; p < n_parts; p += kThreads) M = fmaxf(M, pm[p * stride]);
-  M = block_max(M, s_red);
+  for (int p = t + RT; p < n_parts; p += RT) M = fmaxf(M, pm[p * stride]);
+  M = row_max<RT>(M, s_red);
 
   const int q = t % Q, slot = t / Q;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (M != -INFINITY) {                            // uniform
-    for (int p0 = 0; p0 < n_parts; p0 += kThreads) {
+  if (M != -INFINITY) {                            // uniform over the row
+    for (int p0 = 0; p0 < n_parts; p0 += RT) {
       const int p = p0 + t;
       float w = 0.f;
       if (p0 == 0) w = fast_exp2(m_own - M) * l_own;
       else if (p < n_parts) w = fast_exp2(pm[p * stride] - M) * pl[p * stride];
       den += w;
       s_w[t] = w;
-      __syncthreads();
-      const int n = min(kThreads, n_parts - p0);
+      row_sync<RT>();
+      const int n = min(RT, n_parts - p0);
       const float* o0 = rec0 + (int64_t)p0 * stride + hh * D + 4 * q;
 #pragma unroll 4
       for (int i = slot; i < n; i += kSlots) {
@@ -911,18 +935,18 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
         const float wi = s_w[i];
         num += wi * o;
       }
-      __syncthreads();
+      row_sync<RT>();
     }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
   if ((t & (kWave - 1)) == 0) s_red[t / kWave] = den;
   s_acc[t] = num;
-  __syncthreads();
+  row_sync<RT>();
   if (slot == 0) {
     float dsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) dsum += s_red[w];
+    for (int w = 0; w < kWavesPer; ++w) dsum += s_red[w];
 #pragma unroll
     for (int k = 1; k < kSlots; ++k) num += s_acc[k * Q + q];
     OutT* out = reinterpret_cast<OutT*>(a.out) + row * D + 4 * q;
@@ -931,13 +955,26 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   }
 }
 
+// Rows of the combine kernel at or above which, with few partitions per row,
+// one wavefront per row beats a workgroup per row (measured: 8192 rows of
+// 2..8 partitions 6-7 us faster; 1024 rows of ~40 partitions 13 us slower).
+constexpr int64_t kWaveRowsMin = 4096;
+constexpr int32_t kWaveRowsMaxParts = 32;
+
 template <class Tag, int D, class OutT, bool P8>
 static pa_status launch(const DecodeArgs& a, int64_t units, size_t lds, hipStream_t stream) {
   decode_kernel<Tag, D, OutT, P8><<<(unsigned)units, kThreads, lds, stream>>>(a);
   pa_status st = launch_status();
   if (st != PA_OK || (a.num_parts <= 1 && !a.planned)) return st;
   const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
-  reduce_kernel<D, OutT><<<(unsigned)rows, kThreads, 0, stream>>>(a);
+  // Partitions per row: planned splits give num_parts units per KV head to
+  // num_seqs sequences.
+  const int64_t per_row = a.planned ? (a.num_parts + (int64_t)a.num_seqs - 1) / a.num_seqs
+                                    : a.num_parts;
+  if (rows >= kWaveRowsMin && per_row <= kWaveRowsMaxParts)
+    reduce_kernel<D, OutT, kWave><<<(unsigned)((rows + kWaves - 1) / kWaves), kThreads, 0, stream>>>(a);
+  else
+    reduce_kernel<D, OutT, kThreads><<<(unsigned)rows, kThreads, 0, stream>>>(a);
   return launch_status();
 }
 

@@ -8,7 +8,8 @@ least 512 tokens) that keeps one KV head's units within its share of the
 resident workgroups.  The cases cover every pool dtype, head dims 64 and 128,
 block sizes 8, 16 and 32 (8-token blocks pair up into 16-token tiles), more
 than 64 sequences (the plan's scans then take several rounds), batches whose
-plan collapses to one unit per sequence, zero-length rows, and the fused step.
+plan collapses to one unit per sequence, enough rows for the combine kernel's
+one-wavefront-per-row form, zero-length rows, and the fused step.
 Each output is checked against the fp64 oracle (1e-5 per row for fp32 pools,
 2e-3 otherwise) and against the unsplit kernel (partition_size 0).
 """
@@ -59,6 +60,8 @@ CASES = {
     "bf16-70seqs": lambda: W.scaled("as-70", 209, 70, 1, 2600, 4, 1, 128, "bf16"),
     # 90 x 8 units just under 768 resident: the plan keeps one unit per sequence
     "bf16-90seqs-no-room": lambda: W.scaled("as-90", 210, 90, 600, 2000, 32, 8, 128, "bf16"),
+    # 64 x 64 = 4096 rows of about 1.5 units: combined one wavefront per row
+    "bf16-64seqs-4096rows": lambda: W.scaled("as-64", 214, 64, 600, 3000, 64, 8, 128, "bf16"),
     # one long sequence over many units
     "bf16-one-long": lambda: W.independent("as-one", 211, "bf16", [20011], 16, 2, 128,
                                            _blocks([20011], 16)),

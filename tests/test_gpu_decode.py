@@ -181,6 +181,43 @@ def test_gqa_batch256_full_size_sampled(ps):
     assert err <= 2e-3
 
 
+MANY_ROWS = {
+    # 256 x 32 = 8192 rows of up to 8 partitions: one wavefront per row combines them
+    "gqa-bf16-b256-ps256": (W.gqa_bf16, 256, torch.float32),
+    "gqa-bf16-b256-ps512-bf16out": (W.gqa_bf16, 512, torch.bfloat16),
+    # 256 x 16 = 4096 rows, head_dim 64, up to 10 partitions of 32 tokens
+    "f16-d64-4096rows": (lambda: W.scaled("mr64", 79, 256, 20, 300, 16, 2, 64, "f16"), 32,
+                         torch.float32),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_ROWS))
+def test_many_rows_split_matches_unsplit(name):
+    """Every row of a many-row split (the combine kernel's one-wavefront-per-row
+    form) against the unsplit kernel, and sampled rows against the oracle."""
+    make, ps, odt = MANY_ROWS[name]
+    w = make()
+    batch = build_batch(w, drop_payload_cache=False)
+    got = DecodeStep(batch, partition_size=ps, out_dtype=odt)().float().cpu().numpy()
+    whole = DecodeStep(batch, partition_size=0, out_dtype=torch.float32)().cpu().numpy()
+    assert w.num_seqs * w.num_q_heads >= 4096
+    assert np.isfinite(got).all()
+    if odt == torch.float32:
+        assert row_rel_err(got.astype(np.float64), whole.astype(np.float64)) <= 1e-5
+    else:                                           # a rounding of a value within 1e-5
+        want = torch.from_numpy(whole).to(odt).float().numpy()
+        ulp = np.abs(want) * 2.0 ** -7 + 1e-30
+        assert (np.abs(got - whole) <= ulp + 1e-5 * np.abs(whole).max(axis=-1, keepdims=True)).all()
+    # vs the oracle: the fp32-output split (the same combine path; a 16-bit
+    # output adds its own rounding, checked above)
+    got32 = got if odt == torch.float32 else \
+        DecodeStep(batch, partition_size=ps, out_dtype=torch.float32)().cpu().numpy()
+    rows = [0, 3, w.num_seqs // 2, w.num_seqs - 1]
+    err = row_rel_err(got32[rows].astype(np.float64), OracleRun(w).decode(rows=rows))
+    announce(f"{name}: sampled rows max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
+
+
 def _poison_current_tokens(batch):
     """Overwrite every sequence's current token (position L-1) in the pool with NaN."""
     w = batch.w
