@@ -86,6 +86,24 @@ def test_auto_split_matches_oracle_and_unsplit(name, fused):
     assert row_rel_err(got, whole) <= 1e-5
 
 
+def test_auto_split_long_row_past_one_chunk():
+    """One 40000-token sequence among 255 of 50 tokens, one KV head, 16 query
+    heads: 4096 rows, so the combine kernel runs one wavefront per row, and the
+    long sequence's 79 units take it past its first 64 partitions."""
+    lens = [50] * 256
+    lens[77] = 40000
+    w = W.independent("as-chunk", 215, "bf16", lens, 16, 1, 128, _blocks(lens, 16))
+    batch = build_batch(w, drop_payload_cache=False)
+    got = DecodeStep(batch, partition_size=AUTO, fused=True)().cpu().numpy().astype(np.float64)
+    whole = DecodeStep(batch, partition_size=0, fused=False)().cpu().numpy().astype(np.float64)
+    rows = [0, 76, 77, 78, 255]
+    err = row_rel_err(got[rows], OracleRun(w).decode(rows=rows))
+    announce(f"long row among short ones: max row rel err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= 2e-3
+    assert row_rel_err(got, whole) <= 1e-5
+
+
 def test_auto_split_zero_length_rows_and_clipping():
     """Zero-length rows come out zero, lengths above max_context_len are clipped,
     and both count as the plan's units without disturbing the other rows."""

@@ -75,6 +75,20 @@ def test_split_context_matches_oracle_and_unsplit(ps):
     assert row_rel_err(got, whole.cpu().numpy().astype(np.float64)) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_more_partitions_than_one_chunk(dtype):
+    """16-token partitions over up to 5000 tokens: 313 partitions in a row, so
+    the combine kernel's workgroup walks them in two chunks of 256."""
+    lens = [5000, 4100, 300, 17]
+    w = W.independent(f"ps16-{dtype}", 69, dtype, lens, 8, 2, 128, sum(-(-L // 16) for L in lens) + 4)
+    got, ref, batch, _ = _run(w, partition_size=16)
+    err = row_rel_err(got, ref)
+    announce(f"313 partitions {dtype}: max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
+    whole = DecodeStep(batch, partition_size=0)().cpu().numpy().astype(np.float64)
+    assert row_rel_err(got, whole) <= 1e-5
+
+
 def test_split_context_fp32():
     w = W.scaled("split32", 62, 3, 40, 300, 4, 2, 64, "f32")
     got, ref, _, _ = _run(w, partition_size=64)
