@@ -226,7 +226,11 @@ PA_API pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_
  *                     (pa_decode_workspace_size with the same arguments on the
  *                     same device gives the matching workspace)
  *   workspace         device, >= pa_decode_workspace_size bytes (may be NULL
- *                     when that size is 0)
+ *                     when that size is 0), 16-byte aligned; holds the
+ *                     partial records (and, for a planned split, two ints per
+ *                     sequence) of this call until its kernels finish in
+ *                     stream order: calls that may overlap need separate
+ *                     workspaces; its contents need no initialisation
  * Accumulation is fp32 in every dtype; q.k products of f16/bf16 inputs are
  * exact in fp32.
  */
