@@ -66,6 +66,17 @@ def test_workspace_size_host_only():
     assert st == B.PA_OK and n == 8 * (1024 // 8) * rec * 4 + 16 * 8   # FP8: 4 waves per SIMD
     st, n = B.pa_decode_workspace_size(d, 16, 64, 512, auto)
     assert st == B.PA_OK and n == 0                # nothing longer than one 512-token unit
+    # the planned split starts below one (sequence, KV head) pair per resident
+    # workgroup: 256 compute units x 3 (16-bit), x 4 (FP8), x 2 (fp32, d = 128)
+    for desc, slots in ((d, 768), (d8, 1024), (_desc(dtype="f32"), 512)):
+        below = slots // 8 - 1                     # 8 KV heads
+        st, n = B.pa_decode_workspace_size(desc, below, 64, 4096, auto)
+        assert st == B.PA_OK and n == 8 * (slots // 8) * rec * 4 + below * 8
+        st, n = B.pa_decode_workspace_size(desc, slots // 8, 64, 4096, auto)
+        assert st == B.PA_OK and n == 0            # the pairs already fill the GPU
+    st, n = B.pa_decode_workspace_size(_desc(num_kv_heads=1), 5, 16, 100000, auto)
+    rec16 = (16 * 128 + 2 * 16 + 31) // 32 * 32
+    assert st == B.PA_OK and n == 768 * rec16 * 4 + 5 * 8     # one KV head: all 768 units
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, -2)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(d, 16, 64, 32768, 500)[0] == B.PA_ERR_INVALID_ARG
     assert B.pa_decode_workspace_size(_desc(head_dim=96), 1, 8, 16, 0)[0] == B.PA_ERR_UNSUPPORTED
