@@ -53,6 +53,7 @@ def _workloads():
         "shared-prefix-bf16-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
                                      "1016-token prompt + tails uniform 1..512"),
         "long-ctx-splitk-bf16": (W.long_ctx_bf16, -1, "uniform int 8192..32768"),
+        "long-ctx-1x32k-bf16": (W.long_ctx_single_bf16, -1, "one sequence of 32768 tokens"),
         "gqa-fp8-b256": (W.gqa_fp8, 0, "uniform int 200..2000, FP8 E4M3 cache"),
         "gqa-bf16-b256-in-order": (W.gqa_bf16_in_order, 0,
                                    "uniform int 200..2000, consecutive physical blocks"),

@@ -449,6 +449,14 @@ def long_ctx_bf16(num_seqs: int = 16, seed: int = 5, partition_size: int = 512) 
                        _pool_for(lengths, 16, 0.0), partition_size=partition_size)
 
 
+def long_ctx_single_bf16(length: int = 32768, seed: int = 9) -> Workload:
+    """Single-sequence long-context decode (the latency case): one sequence of
+    32768 tokens, 64 q / 8 kv heads x 128, bf16; too few (sequence, KV head)
+    pairs to fill the GPU, so the split is planned from the length."""
+    return independent("long-ctx-1x32k-bf16", seed, "bf16", [length], 64, 8, 128,
+                       _pool_for([length], 16, 0.0), partition_size=-1)
+
+
 def scaled(kind: str, seed: int, num_seqs: int, lo: int, hi: int, num_q_heads: int,
            num_kv_heads: int, head_dim: int, dtype: str, extra_blocks: float = 0.1,
            partition_size: int = 0, block_size: int = 16) -> Workload:
