@@ -909,13 +909,27 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   const float* pm = rec0 + G * D + hh;             // m of partition p at pm[p * stride]
   const float* pl = pm + G;
 
+  // This thread's slices of its first kPre partitions do not depend on the
+  // row's maximum: they are loaded together with (m, l), one round trip.
+  const int q = t % Q, slot = t / Q;
+  constexpr int kPre = 8;
+  f32x4 pre[kPre];
+  {
+    const int n0 = min(RT, n_parts);
+    const float* ob = rec0 + hh * D + 4 * q;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int i = slot + k * kSlots;
+      pre[k] = i < n0 ? *reinterpret_cast<const f32x4*>(ob + (int64_t)i * stride)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   const float m_own = t < n_parts ? pm[t * stride] : -INFINITY;
   const float l_own = t < n_parts ? pl[t * stride] : 0.f;
   float M = m_own;
   for (int p = t + RT; p < n_parts; p += RT) M = fmaxf(M, pm[p * stride]);
   M = row_max<RT>(M, s_red);
 
-  const int q = t % Q, slot = t / Q;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (M != -INFINITY) {                            // uniform over the row
@@ -928,9 +942,15 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
       s_w[t] = w;
       row_sync<RT>();
       const int n = min(RT, n_parts - p0);
+      int i = slot;
+      if (p0 == 0) {
+#pragma unroll
+        for (int k = 0; k < kPre; ++k, i += kSlots)
+          if (i < n) num += s_w[i] * pre[k];
+      }
       const float* o0 = rec0 + (int64_t)p0 * stride + hh * D + 4 * q;
 #pragma unroll 4
-      for (int i = slot; i < n; i += kSlots) {
+      for (; i < n; i += kSlots) {
         const f32x4 o = *reinterpret_cast<const f32x4*>(o0 + (int64_t)i * stride);
         const float wi = s_w[i];
         num += wi * o;
