@@ -148,6 +148,51 @@ def test_random_scripts_read_equals_script_contents():
             assert got[:len(rows)] == rows
 
 
+def test_block_copy_carries_every_slot_including_the_last():
+    """Copy-on-write as the device does it: the private copy takes all b slots
+    of the shared block, tokens and unused slots alike, then the new token
+    overwrites its own slot.  Worked by hand on a 3-block pool of width 4 whose
+    blocks first served released tenants (their tokens stay in the slots):
+
+      old = o0..o3 -> block 2 (end of [0, 1, 2]);  x = x0..x3 -> block 1
+      release x, then old: free list [0, 1, 2]
+      A = a0 a1    -> block 2: [a0, a1, o2, o3]  (o2, o3 are stale)
+      fork B; B appends b2: block 2 is shared and partial, so block 1 (end of
+      [0, 1]) receives the whole of block 2 -- o3 replaces x3 in the last slot
+      -- and b2 goes to offset 2: [a0, a1, b2, o3].
+    """
+    m = BlockModel(3, 4, free_order=[0, 1, 2])
+    m.create("old", ["o0", "o1", "o2", "o3"])
+    m.create("x", ["x0", "x1", "x2", "x3"])
+    m.release("x")
+    m.release("old")
+    m.create("A", ["a0", "a1"])
+    m.fork("A", "B")
+    assert m.append("B", "b2") == (2, 1)
+    p = SlotPool(3, 4)
+    p.replay(m.events)
+    assert p.block_payloads(2) == ["a0", "a1", "o2", "o3"]
+    assert p.block_payloads(1) == ["a0", "a1", "b2", "o3"]
+    assert p.block_payloads(0) == [None] * 4
+    assert m.read("A") == ["a0", "a1"] and m.read("B") == ["a0", "a1", "b2"]
+
+    # Second case: the shared block was never full (slots 2, 3 never written),
+    # the destination held a released tenant.  The copy carries the unwritten
+    # slots too, so nothing of the tenant survives:
+    #   x = x0..x3 -> block 2; A = a0 a1 -> block 1; release x: free [0, 2]
+    #   fork B; B appends b2: block 2 <- block 1 = [a0, a1, -, -], then b2.
+    m = BlockModel(3, 4, free_order=[0, 1, 2])
+    m.create("x", ["x0", "x1", "x2", "x3"])
+    m.create("A", ["a0", "a1"])
+    m.release("x")
+    m.fork("A", "B")
+    assert m.append("B", "b2") == (1, 2)
+    p = SlotPool(3, 4)
+    p.replay(m.events)
+    assert p.block_payloads(1) == ["a0", "a1", None, None]
+    assert p.block_payloads(2) == ["a0", "a1", "b2", None]
+
+
 def test_shared_prefix_copy_count():
     """Prompt 1016 = 63 full blocks + 8 tokens: of 8 forks, the first 7 appends copy
     the shared partial block and the 8th writes in place (the page warns that a

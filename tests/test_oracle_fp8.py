@@ -8,7 +8,11 @@
     inside the finite range (the tie rule);
   * saturation and NaN handling;
   * the array form equals the scalar definition;
-  * error bound: a normal-range quotient is within 2^-4 relative of its code.
+  * error bound: a normal-range quotient is within 2^-4 relative of its code;
+  * per-head scales (scales other than 1): a value stored under scale s and
+    read back is within 2^-4 relative of itself; the code is the library's
+    conversion of the fp32 quotient x / s; saturation reads back as exactly
+    +-448 s.
 """
 import math
 
@@ -81,3 +85,46 @@ def test_relative_error_bound_in_normal_range():
     y = rng.uniform(2.0 ** -6, 448, 20000).astype(np.float32) * rng.choice([-1, 1], 20000)
     back = F8.dequantize(F8.quantize(y, 1.0), 1.0)
     assert np.all(np.abs(back - y) <= 2.0 ** -4 * np.abs(y))
+
+
+SCALES = (0.0107, 3.0 / 448, 0.37, 2.5)
+
+
+def _quotients_in_normal_range(rng, n):
+    """Target quotients x/s spread over E4M3's normal range, both signs."""
+    mag = np.exp(rng.uniform(np.log(2.0 ** -6 * 1.01), np.log(440.0), n))
+    return mag * rng.choice([-1.0, 1.0], n)
+
+
+def test_scaled_round_trip_within_bound():
+    """A value stored under scale s and read back is the value within the
+    format's half-step: |dequantize(quantize(x, s), s) - x| <= 2^-4 |x| (plus
+    the fp32 rounding of the quotient) wherever x / s is a normal E4M3
+    magnitude.  Any scale misuse (ignored, inverted, applied twice) is off by
+    a factor s or s^2."""
+    rng = np.random.default_rng(3)
+    for s in SCALES:
+        x = (_quotients_in_normal_range(rng, 20000) * s).astype(np.float32)
+        back = F8.dequantize(F8.quantize(x, s), s)
+        xd = x.astype(np.float64)
+        assert np.all(np.abs(back - xd) <= (2.0 ** -4 + 2.0 ** -22) * np.abs(xd)), s
+
+
+def test_scaled_codes_equal_library_conversion_of_the_quotient():
+    """The stored code is torch's float8_e4m3fn conversion of the fp32 quotient
+    x / s (a library routine for the rounding, with the division done in fp32)."""
+    rng = np.random.default_rng(4)
+    for s in SCALES:
+        x = (rng.normal(0, 150, 20000) * s).astype(np.float32)
+        q = x / np.float32(s)
+        inside = np.abs(q) <= 448                 # torch saturates nothing: keep the finite range
+        assert np.array_equal(F8.quantize(x[inside], s), _torch_codes(q[inside]))
+
+
+def test_scaled_saturation_lands_on_448_times_scale():
+    """Beyond the largest code, a stored value reads back as exactly +-448 s."""
+    for s in SCALES:
+        s32 = float(np.float32(s))
+        big = np.array([448 * s * 1.5, -448 * s * 4, 1e30, -1e30], dtype=np.float32)
+        back = F8.dequantize(F8.quantize(big, s), s)
+        assert back.tolist() == [448 * s32, -448 * s32, 448 * s32, -448 * s32]

@@ -11,6 +11,7 @@ import oracle.allocator as OAL
 import oracle.attention as OA
 import oracle.paging as OP
 import oracle.fp8 as OF8
+import oracle.pool as OPL
 import oracle.prefill as OPF
 from tests import test_oracle_allocator as TAL
 from tests import test_oracle_attention as TAT
@@ -54,6 +55,14 @@ def _fp8_pins():
     TF8.test_matches_library_conversion_including_ties()
     TF8.test_saturation_and_nan()
     TF8.test_relative_error_bound_in_normal_range()
+    TF8.test_scaled_round_trip_within_bound()
+    TF8.test_scaled_codes_equal_library_conversion_of_the_quotient()
+    TF8.test_scaled_saturation_lands_on_448_times_scale()
+
+
+def _pool_pins():
+    TAL.test_block_copy_carries_every_slot_including_the_last()
+    TAL.test_random_scripts_read_equals_script_contents()
 
 
 def _allocator_pins():
@@ -147,30 +156,32 @@ def _waste_wrong(T, b):
     return T % b
 
 
-def _append_no_cow(self, name, payload):
+def _grow_no_cow(self, name, payload):
     table = self.tables[name]
-    last = table[-1]
-    if len(self.contents[last]) == self.width:
-        if not self.free:
-            raise MemoryError("full")
-        table.append(self._fresh_block())
-    self._put(table[-1], payload)
-    self._verify()
+    j, offset = divmod(self.length(name), self.width)
+    if offset == 0:
+        self._set_entry(table, j, self._claim())
+    self._place(table[j], payload)                    # shared block written in place
     return None
 
 
-def _fresh_from_front(self):
-    blk = self.free.pop(0)
-    self.refcount[blk] = 1
-    self.contents[blk] = []
+def _claim_from_front(self):
+    if not self.free:
+        raise MemoryError("full")
+    blk = self.free.pop(0)                            # front of the free list
+    stale = self.contents[blk]
+    self.refcount[blk], self.contents[blk] = 1, []
+
+    def undo():
+        self.refcount[blk], self.contents[blk] = 0, stale
+        self.free.insert(0, blk)
+    self._undo.append(undo)
     return blk
 
 
-def _unref_no_free(self, blk):
+def _drop_ref_never_frees(self, blk):
     self.refcount[blk] -= 1
-    if self.refcount[blk] == 0:
-        self.contents[blk] = []
-
+    self._undo.append(lambda: self.refcount.__setitem__(blk, self.refcount[blk] + 1))
 
 def _chunk_excludes_own_position(q_rows, K, V, scale):
     n, L = q_rows.shape[0], K.shape[0]
@@ -198,53 +209,41 @@ def _chunk_sees_next_position(q_rows, K, V, scale):
 
 
 def _swap_in_reversed(self, name):
-    host_table = self.swapped[name]
-    if len(host_table) > len(self.free):
-        raise MemoryError("pool full")
-    table, pairs = [], []
-    for hb in reversed(host_table):                   # blocks restored in the wrong order
-        blk = self._fresh_block()
-        self.contents[blk] = list(self.host_contents[hb])
-        self.events.append(("swap_in", hb, blk))
-        pairs.append((hb, blk))
-        table.append(blk)
-    for hb in host_table:
-        self.host_contents[hb] = []
-        self.host_free.append(hb)
-    del self.swapped[name]
-    self.tables[name] = table
-    return pairs
+    with self._atomic():
+        host_table = self.swapped[name]
+        table = []
+        for hb in reversed(host_table):               # blocks restored in the wrong order
+            blk = self._claim()
+            self._fill(blk, list(self.host_contents[hb]))
+            self._record("swap_in", hb, blk)
+            table.append(blk)
+        for hb in host_table:
+            self._return_host(hb)
+        self._set_swapped(name, None)
+        self._set_table(name, table)
+        return []
 
 
 def _swap_out_keeps_device_blocks(self, name):
-    table = self.tables[name]
-    if len(table) > len(self.host_free):
-        raise MemoryError("host swap space full")
-    host_table = []
-    for blk in table:
-        hb = self.host_free.pop()
-        self.host_contents[hb] = list(self.contents[blk])
-        self.events.append(("swap_out", blk, hb))
-        host_table.append(hb)
-    self.tables.pop(name)                             # references never dropped
-    self.swapped[name] = host_table
-    return []
+    with self._atomic():
+        table = self.tables[name]
+        host_table = []
+        for blk in table:
+            hb = self._claim_host()
+            self._set_host(hb, list(self.contents[blk]))
+            self._record("swap_out", blk, hb)
+            host_table.append(hb)
+        self._set_table(name, None)                   # references never dropped
+        self._set_swapped(name, host_table)
+        return []
 
 
-def _swap_out_host_front(self, name):
-    table = self.tables[name]
-    if len(table) > len(self.host_free):
-        raise MemoryError("host swap space full")
-    host_table = []
-    for blk in table:
-        hb = self.host_free.pop(0)                    # front of the host free list
-        self.host_contents[hb] = list(self.contents[blk])
-        self.events.append(("swap_out", blk, hb))
-        host_table.append(hb)
-    for blk in self.tables.pop(name):
-        self._unref(blk)
-    self.swapped[name] = host_table
-    return []
+def _claim_host_from_front(self):
+    if not self.host_free:
+        raise MemoryError("no free host block")
+    hb = self.host_free.pop(0)                        # front of the host free list
+    self._undo.append(lambda: self.host_free.insert(0, hb))
+    return hb
 
 
 def _fp8_quantize_ties_away(x, scale):
@@ -279,6 +278,32 @@ def _fp8_decode_bias8(code):
     return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)
 
 
+def _fp8_dequantize_ignores_scale(codes, scale):
+    return OF8.TABLE[np.asarray(codes, dtype=np.int64)]
+
+
+def _fp8_dequantize_divides_by_scale(codes, scale):
+    return OF8.TABLE[np.asarray(codes, dtype=np.int64)] / float(np.float32(scale))
+
+
+def _fp8_quantize_multiplies_by_scale(x, scale):
+    y = np.asarray(x, dtype=np.float32) * np.float32(scale)
+    return np.asarray([OF8.encode(float(v)) for v in y.ravel()], dtype=np.uint8).reshape(y.shape)
+
+
+def _pool_copy_drops_last_slot(self, src, dst):
+    b = self.width
+    self.slots[dst * b:(dst + 1) * b - 1] = self.slots[src * b:(src + 1) * b - 1]
+
+
+def _pool_copy_filled_prefix_only(self, src, dst):
+    b = self.width
+    for o in range(b):
+        if self.slots[src * b + o] is None:
+            break
+        self.slots[dst * b + o] = self.slots[src * b + o]
+
+
 MUTANTS = [
     ("softmax drops the scale", OA, "softmax_attention", _softmax_no_scale, _attention_pins),
     ("K and V swapped", OA, "softmax_attention", _softmax_kv_swapped, _attention_pins),
@@ -291,15 +316,20 @@ MUTANTS = [
     ("offset off by one", OP, "logical_address", _address_off_by_one, _paging_pins),
     ("slot with block and offset swapped", OP, "slot", _slot_transposed, _paging_pins),
     ("waste as T mod b", OP, "tail_waste", _waste_wrong, _paging_pins),
-    ("append without copy-on-write", OAL.BlockModel, "append", _append_no_cow, _allocator_pins),
-    ("take from the front of the free list", OAL.BlockModel, "_fresh_block", _fresh_from_front, _allocator_pins),
-    ("freed blocks never return", OAL.BlockModel, "_unref", _unref_no_free, _allocator_pins),
+    ("append without copy-on-write", OAL.BlockModel, "_grow", _grow_no_cow, _allocator_pins),
+    ("take from the front of the free list", OAL.BlockModel, "_claim", _claim_from_front, _allocator_pins),
+    ("freed blocks never return", OAL.BlockModel, "_drop_ref", _drop_ref_never_frees, _allocator_pins),
     ("swap-in restores blocks in reverse order", OAL.BlockModel, "swap_in", _swap_in_reversed, _swap_pins),
     ("swap-out keeps the device references", OAL.BlockModel, "swap_out", _swap_out_keeps_device_blocks, _swap_pins),
-    ("swap-out takes host blocks from the front", OAL.BlockModel, "swap_out", _swap_out_host_front, _swap_pins),
+    ("swap-out takes host blocks from the front", OAL.BlockModel, "_claim_host", _claim_host_from_front, _swap_pins),
     ("fp8 ties rounded away from zero", OF8, "quantize", _fp8_quantize_ties_away, _fp8_pins),
     ("fp8 rounding truncates", OF8, "quantize", _fp8_quantize_truncate, _fp8_pins),
     ("fp8 exponent bias 8", OF8, "decode", _fp8_decode_bias8, _fp8_pins),
+    ("fp8 read-back ignores the scale", OF8, "dequantize", _fp8_dequantize_ignores_scale, _fp8_pins),
+    ("fp8 read-back divides by the scale", OF8, "dequantize", _fp8_dequantize_divides_by_scale, _fp8_pins),
+    ("fp8 store multiplies by the scale", OF8, "quantize", _fp8_quantize_multiplies_by_scale, _fp8_pins),
+    ("block copy drops each block's last slot", OPL.SlotPool, "copy", _pool_copy_drops_last_slot, _pool_pins),
+    ("block copy stops at the first unwritten slot", OPL.SlotPool, "copy", _pool_copy_filled_prefix_only, _pool_pins),
     ("causal mask excludes the row's own position", OPF, "causal_chunk", _chunk_excludes_own_position, _prefill_pins),
     ("chunk positions counted from the chunk start", OPF, "causal_chunk", _chunk_positions_from_chunk_start, _prefill_pins),
     ("causal mask lets a row see the next position", OPF, "causal_chunk", _chunk_sees_next_position, _prefill_pins),
