@@ -43,9 +43,9 @@
  *     given: a table entry outside [0, num_blocks) contributes no tokens, a
  *     slot outside the pool is skipped, a length larger than the table or the
  *     stated maximum is clipped.  Results for such inputs are unspecified;
- *     pa_validate_tables reports them ("Before a real kernel consumes a
- *     table, validate ownership, bounds, cache dtype and logical length",
- *     "Inside vLLM and TGI", same section).
+ *     pa_validate_tables reports them (the pages ask for a debug check of
+ *     tables, bounds and lengths before a kernel reads them: "Inside vLLM
+ *     and TGI", same section, validation paragraph).
  *
  * Pool layout (the ABI of the cache; chosen for gfx950, see each kernel)
  *   Two separate pools, K and V, each num_blocks * Hkv tiles of

@@ -603,10 +603,25 @@ void decode_kernel(DecodeArgs a) {
   const int G = a.group;
   const int head0 = g * G;
 
+  const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
+  // Fused step: the current token sits at position lens[seq] - 1, which the
+  // three-call form (slot mapping, write, attention) writes whenever the
+  // table row reaches it -- also when that position lies beyond the attended
+  // length L (a length clipped to max_len).  It joins the attention only when
+  // it is attended, i.e. when the length was not clipped.
+  const int raw_len = a.k_new != nullptr ? a.lens[seq] : 0;
+  const bool store_new = raw_len >= 1 && (raw_len - 1) / a.block_size < a.max_blocks;
+  const bool patch_new = store_new && raw_len == L;
+  NewToken<Tag, D> tok;
+
   if (L == 0) {                                  // no tokens: zero output row
     if (part == 0) {
       OutT* o = reinterpret_cast<OutT*>(a.out) + ((int64_t)seq * a.num_q_heads + head0) * D;
       for (int i = threadIdx.x; i < G * D; i += kThreads) store_out<OutT>(o + i, 0.f);
+      if (store_new) {                           // a length clipped to zero: still written
+        tok.load(a, seq, g);
+        tok.store(a, trow, (raw_len - 1) / a.block_size, g, (raw_len - 1) % a.block_size);
+      }
     }
     put_header();
     return;
@@ -643,20 +658,20 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* trow = a.tables + (int64_t)seq * a.max_blocks;
   const int64_t head_tile = (int64_t)g * tile_bytes;
   const int64_t block_stride = (int64_t)a.num_kv_heads * tile_bytes;
 
-  // Fused step: the unit holding position L-1 writes the current token.
-  const int j_new = (L - 1) / rows;            // its tile
+  // Fused step: the unit holding the last attended tile writes the current
+  // token (and, when it is attended, at position L-1, patches it in).
+  const int j_new = (L - 1) / rows;            // the tile of position L-1
   int o_new = (L - 1) % rows;                  // its register row
-  const bool own_new = a.k_new != nullptr && j_new >= j0 && j_new < j1;
-  if (P8 && own_new && o_new >= 8) {           // in block b: it moves up when block a is out
+  const bool own_new = store_new && j_new >= j0 && j_new < j1;
+  const bool own_patch = own_new && patch_new;
+  if (P8 && own_patch && o_new >= 8) {         // in block b: it moves up when block a is out
     const int pa_ = trow[2 * j_new];          // of the pool (valid blocks are packed first)
     if (pa_ < 0 || pa_ >= a.num_blocks) o_new -= 8;
   }
   char* stage = reinterpret_cast<char*>(smem) + a.stage_off;
-  NewToken<Tag, D> tok;
   if (own_new) tok.load(a, seq, g);             // in flight with the first blocks
 
   // Blocks are processed in chunks of up to 64 per wavefront: one table load
@@ -730,7 +745,7 @@ void decode_kernel(DecodeArgs a) {
       const int ca = oka ? min(8, L - 16 * j) : 0;
       const int cb = okb ? min(8, L - 16 * j - 8) : 0;
       int c = ca + cb;
-      if (own_new && j == j_new) c = -c;
+      if (own_patch && j == j_new) c = -c;
       d_nv = c;
       const int first_blk = oka ? pa_ : (okb ? pb_ : 0);
       const int second_blk = oka && okb ? pb_ : 0;
@@ -745,7 +760,7 @@ void decode_kernel(DecodeArgs a) {
       const int phys = lane < n ? trow[j >> sub_shift] : -1;
       const bool ok = phys >= 0 && phys < a.num_blocks;
       int c = ok ? min(a.rows, L - j * a.rows) : 0;
-      if (own_new && j == j_new) c = -c;
+      if (own_patch && j == j_new) c = -c;
       d_nv = c;
       const uint64_t addr = k_base + (uint64_t)(ok ? phys : 0) * (uint64_t)block_stride +
                             (uint64_t)head_tile + (uint64_t)(j & (a.sub - 1)) * (uint64_t)sub_bytes;
@@ -757,7 +772,7 @@ void decode_kernel(DecodeArgs a) {
   };
 
   if (cnt > 0) open_chunk();
-  if (own_new) {                                // every wavefront reaches this barrier
+  if (own_patch) {                              // every wavefront reaches this barrier
     tok.stage(stage);
     __syncthreads();
   }
@@ -781,7 +796,8 @@ void decode_kernel(DecodeArgs a) {
   }
   // Pool write of the current token after the loop: a store while the same
   // tile streams in makes those loads wait on it.
-  if (own_new) tok.store(a, trow, (L - 1) / a.block_size, g, (L - 1) % a.block_size);
+  if (own_new)
+    tok.store(a, trow, (raw_len - 1) / a.block_size, g, (raw_len - 1) % a.block_size);
 
   // ---- merge the four wavefronts (LDS) ----
   const float l_tot = xor_sum(st.l);

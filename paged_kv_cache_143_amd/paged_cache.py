@@ -229,7 +229,9 @@ class DecodeStep:
         self.slots = torch.empty(S, dtype=torch.int32, device=dev)
         self.k_new = batch.step_k.to(dev)
         self.v_new = batch.step_v.to(dev)
-        self.out = torch.empty((S, w.num_q_heads, w.head_dim), dtype=out_dtype, device=dev)
+        # NaN until a launch writes it: a row no kernel writes cannot pass for a result
+        self.out = torch.full((S, w.num_q_heads, w.head_dim), float("nan"), dtype=out_dtype,
+                              device=dev)
         nbytes = B.workspace_size(batch.kv.desc, S, w.num_q_heads, batch.max_len, partition_size)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
@@ -287,7 +289,7 @@ class PrefillStep:
             vs.append(v[L - n:L])
         self.k_new = torch.cat(ks).to(dev)
         self.v_new = torch.cat(vs).to(dev)
-        self.out = torch.empty(self.q.shape, dtype=out_dtype, device=dev)
+        self.out = torch.full(self.q.shape, float("nan"), dtype=out_dtype, device=dev)
 
     def write_chunks(self) -> None:
         B.slot_mapping_t(self.b.tables, self.seq_ids, self.positions, self.slots,

@@ -86,3 +86,16 @@ class OracleRun:
 
     def copies(self):
         return [(a, b) for kind, a, b in self.model.events if kind == "copy"]
+
+
+_FULL_DECODE: Dict[tuple, np.ndarray] = {}
+
+
+def full_decode(w) -> np.ndarray:
+    """Every row of the oracle's decode of workload `w` ([S][Hq][d] fp64),
+    computed once per workload per test session (several launch
+    configurations of one batch compare against the same rows)."""
+    key = (w.name, w.seed, w.dtype, w.block_size, w.num_seqs, w.num_blocks)
+    if key not in _FULL_DECODE:
+        _FULL_DECODE[key] = OracleRun(w).decode()
+    return _FULL_DECODE[key]

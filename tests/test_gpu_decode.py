@@ -5,9 +5,10 @@ Tolerance (per row = (sequence, query head): max_d |gpu - ref| / max_d |ref|):
 several tiles and ragged tails, every GQA group size up to 16, head_dim 64
 and 128, NaN poison in unused slots and free blocks, padded table entries,
 recycled blocks with stale tenants, split-context partitions, forks sharing
-blocks before and after copy-on-write, zero-length rows, and the
-batch-256 GQA workload at full size (sampled rows) in the launch
-configuration the benchmark times.
+blocks before and after copy-on-write, zero-length rows, lengths clipped by
+max_context_len in the fused step, and every full-size workload (every row of
+the batch against the oracle) in the launch configuration the benchmark
+times.  Outputs start as NaN, so a row that no kernel writes fails.
 """
 import numpy as np
 import pytest
@@ -17,7 +18,8 @@ from paged_kv_cache_143_amd import binding as B
 from paged_kv_cache_143_amd import workloads as W
 from paged_kv_cache_143_amd.paged_cache import DecodeStep, build_batch
 from tests.gpu_util import announce, require_gpu, row_rel_err, tol_for
-from tests.oracle_glue import OracleRun
+from oracle import attention as OA
+from tests.oracle_glue import OracleRun, full_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -185,13 +187,14 @@ def test_shared_prefix_full_block_prompt():
 
 
 @pytest.mark.parametrize("ps", [0, 256, 512])
-def test_gqa_batch256_full_size_sampled(ps):
-    """The batch-256 GQA bf16 workload at full size, sampled rows vs the oracle."""
+def test_gqa_batch256_full_size_all_rows(ps):
+    """The batch-256 GQA bf16 workload at full size: every row vs the oracle."""
     w = W.gqa_bf16()
-    rows = [0, 1, 37, 100, 128, 200, 254, 255]
-    got, ref, batch, _ = _run(w, partition_size=ps, rows=rows)
-    err = row_rel_err(got, ref)
-    announce(f"gqa-bf16-b256 ps={ps}: rows {rows} max row rel err {err:.3e}")
+    batch = build_batch(w, drop_payload_cache=False)
+    got = DecodeStep(batch, partition_size=ps, fused=False)().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, full_decode(w))
+    announce(f"gqa-bf16-b256 ps={ps}: all {w.num_seqs} rows max row rel err {err:.3e}")
     assert err <= 2e-3
 
 
@@ -208,7 +211,7 @@ MANY_ROWS = {
 @pytest.mark.parametrize("name", list(MANY_ROWS))
 def test_many_rows_split_matches_unsplit(name):
     """Every row of a many-row split (the combine kernel's one-wavefront-per-row
-    form) against the unsplit kernel, and sampled rows against the oracle."""
+    form) against the unsplit kernel and against the oracle."""
     make, ps, odt = MANY_ROWS[name]
     w = make()
     batch = build_batch(w, drop_payload_cache=False)
@@ -222,13 +225,13 @@ def test_many_rows_split_matches_unsplit(name):
         want = torch.from_numpy(whole).to(odt).float().numpy()
         ulp = np.abs(want) * 2.0 ** -7 + 1e-30
         assert (np.abs(got - whole) <= ulp + 1e-5 * np.abs(whole).max(axis=-1, keepdims=True)).all()
-    # vs the oracle: the fp32-output split (the same combine path; a 16-bit
-    # output adds its own rounding, checked above)
+    # vs the oracle, every row: the fp32-output split (the same combine path; a
+    # 16-bit output adds its own rounding, checked above)
     got32 = got if odt == torch.float32 else \
         DecodeStep(batch, partition_size=ps, out_dtype=torch.float32)().cpu().numpy()
-    rows = [0, 3, w.num_seqs // 2, w.num_seqs - 1]
-    err = row_rel_err(got32[rows].astype(np.float64), OracleRun(w).decode(rows=rows))
-    announce(f"{name}: sampled rows max row rel err {err:.3e}")
+    assert np.isfinite(got32).all()
+    err = row_rel_err(got32.astype(np.float64), full_decode(w))
+    announce(f"{name}: all rows max row rel err {err:.3e}")
     assert err <= tol_for(w.dtype)
 
 
@@ -237,7 +240,7 @@ def _poison_current_tokens(batch):
     w = batch.w
     slots = [batch.bm.slot(n, batch.bm.lengths[n] - 1) for n in w.seq_names]
     shape = (len(slots), w.num_kv_heads, w.head_dim)
-    nan = torch.full(shape, float("nan"), dtype=W.DTYPES[w.dtype], device="cuda")
+    nan = torch.full(shape, float("nan"), dtype=W.DTYPES[w.input_dtype], device="cuda")
     batch.kv.write(nan, nan, torch.tensor(slots, dtype=torch.int32, device="cuda"))
 
 
@@ -274,44 +277,80 @@ def test_fused_step_equals_three_calls_and_oracle(name):
     assert err <= tol_for(w.dtype)
 
 
-def test_fused_step_full_size_sampled():
-    """The batch-256 GQA workload in the benchmark's launch configuration."""
+@pytest.mark.parametrize("ps", [0, 32])
+@pytest.mark.parametrize("clip", ["longest", "all", "zero"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_fused_step_with_clipped_lengths(dtype, clip, ps):
+    """Lengths above max_context_len.  The three-call form writes each current
+    token at its true position L_i - 1 (slot mapping + write) and attends the
+    clipped range; the fused step must do the same: bit-identical pools and
+    outputs, and the outputs equal the oracle over the clipped lengths (the
+    current token of a clipped sequence is written but not attended)."""
+    w = W.scaled(f"clip-{dtype}", 76, 6, 20, 200, 8, 2, 128, dtype)
+    lens = [len(r) for r in W.fork_payload_rows(w).values()]
+    cap = {"longest": max(lens) - 7, "all": min(lens) - 3, "zero": 0}[clip]
+    outs, pools = [], []
+    for fused in (False, True):
+        batch = build_batch(w, drop_payload_cache=False)
+        _poison_current_tokens(batch)
+        batch.max_len = cap
+        step = DecodeStep(batch, partition_size=ps, fused=fused)
+        outs.append(step().clone())
+        torch.cuda.synchronize()
+        pools.append((batch.kv.k.clone(), batch.kv.v.clone()))
+    assert torch.equal(outs[0], outs[1])
+    bits = lambda t: t.view(torch.uint8 if t.element_size() == 1 else torch.int16)
+    for a, b in zip(pools[0], pools[1]):
+        assert torch.equal(bits(a), bits(b))
+    # every current token is in the pool (nothing poisoned is left at L_i - 1)
+    run = OracleRun(w)
+    got = outs[1].cpu().numpy().astype(np.float64)
+    clipped = [min(L, cap) for L in run.lengths]
+    ref = OA.paged_decode(run.pool, run.resolve, run.tables, clipped, run.q64(), w.num_kv_heads,
+                          w.scale)
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    announce(f"clipped {dtype} {clip} ps={ps}: max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
+    if clip == "zero":
+        assert (got == 0).all()
+
+
+def test_fused_step_full_size_all_rows():
+    """The batch-256 GQA workload in the benchmark's launch configuration
+    (pa_decode_step, one pass), every row vs the oracle."""
     w = W.gqa_bf16()
     batch = build_batch(w, drop_payload_cache=False)
     _poison_current_tokens(batch)
     out = DecodeStep(batch, partition_size=0, fused=True)().cpu().numpy().astype(np.float64)
-    rows = [0, 3, 64, 127, 128, 191, 250, 255]
-    ref = OracleRun(w).decode(rows=rows)
-    err = row_rel_err(out[rows], ref)
-    announce(f"fused gqa-bf16-b256: max row rel err {err:.3e}")
+    assert np.isfinite(out).all()
+    err = row_rel_err(out, full_decode(w))
+    announce(f"fused gqa-bf16-b256: all rows max row rel err {err:.3e}")
     assert err <= 2e-3
 
 
 FULL = {
-    "opt13b-mha-f16": (W.opt13b_f16, 0, [0, 17, 40, 63], None),
-    "shared-prefix-p1024": (lambda: W.shared_prefix_bf16(prompt_len=1024), 0,
-                            [0, 7, 8, 100, 255], 0),
-    "shared-prefix-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0,
-                            [0, 1, 7, 8, 130, 255], 32 * 7),
-    "gqa-in-order": (W.gqa_bf16_in_order, 0, [0, 100, 255], None),
-    "long-ctx-splitk": (W.long_ctx_bf16, 512, [0, 5, 15], None),
-    "long-ctx-auto": (W.long_ctx_bf16, -1, [1, 9, 14], None),
+    "opt13b-mha-f16": (W.opt13b_f16, 0, None),
+    "shared-prefix-p1024": (lambda: W.shared_prefix_bf16(prompt_len=1024), 0, 0),
+    "shared-prefix-p1016": (lambda: W.shared_prefix_bf16(prompt_len=1016), 0, 32 * 7),
+    "gqa-in-order": (W.gqa_bf16_in_order, 0, None),
+    "long-ctx-splitk": (W.long_ctx_bf16, 512, None),
+    "long-ctx-auto": (W.long_ctx_bf16, -1, None),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_workloads_sampled(name):
+def test_full_size_workloads_all_rows(name):
     """The other workloads at full size, in the benchmark's step (pa_decode_step with
-    the current tokens first poisoned in the pool), sampled rows vs the oracle."""
-    make, ps, rows, copies = FULL[name]
+    the current tokens first poisoned in the pool), every row vs the oracle."""
+    make, ps, copies = FULL[name]
     w = make()
     batch = build_batch(w, drop_payload_cache=False)
     if copies is not None:
         assert len(batch.copies) == copies
     _poison_current_tokens(batch)
     out = DecodeStep(batch, partition_size=ps, fused=True)().cpu().numpy().astype(np.float64)
-    ref = OracleRun(w).decode(rows=rows)
-    err = row_rel_err(out[rows], ref)
-    announce(f"{name} ps={ps}: rows {rows} max row rel err {err:.3e}")
     assert np.isfinite(out).all()
+    err = row_rel_err(out, full_decode(w))
+    announce(f"{name} ps={ps}: all {w.num_seqs} rows max row rel err {err:.3e}")
     assert err <= tol_for(w.dtype)

@@ -15,8 +15,9 @@ SRC = os.path.join(B.CSRC, "pa_decode.hip")
 
 def _kernels(path, tmp_path):
     out = str(tmp_path / "k.s")
-    cmd = [B.hipcc(), "-O3", "-std=c++17", f"--offload-arch={B.ARCH}", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", f"-I{B.INCLUDE}", f"-I{B.CSRC}", "--offload-device-only",
+    # the flags libpa.so is built with (register-form options change the code)
+    flags = [f for f in B.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [B.hipcc(), *flags, f"-I{B.INCLUDE}", f"-I{B.CSRC}", "--offload-device-only",
            "-S", path, "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     text = open(out).read()
