@@ -196,7 +196,100 @@ def cpu_baseline(w, budget_s: float):
                       f"{w.num_seqs}-sequence batch ({tokens} context tokens, all "
                       f"{w.num_q_heads} query heads), fp64 NumPy oracle, 1 thread, "
                       f"{elapsed:.1f} s",
-            "seconds": elapsed, "sequences": done}
+            "seconds": elapsed, "sequences": done,
+            "host_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_worker(job):
+    """One process of the all-core oracle figure: rebuild the workload's pool
+    (untimed), then decode its share of the sequences, one thread, until the
+    budget; returns (KV bytes, oracle seconds, decodes)."""
+    name, share, budget_s = job
+    from threadpoolctl import threadpool_limits
+    import torch
+    from oracle.allocator import run_script
+    from oracle.attention import paged_decode
+    from oracle.pool import SlotPool
+
+    torch.set_num_threads(1)
+    w = _workloads()[name][0]()
+    model = run_script(w.ops, w.num_blocks, w.block_size, w.free_order, checked=False)
+    pool = SlotPool(w.num_blocks, w.block_size)
+    pool.replay(model.events)
+    tables = [model.tables[n] for n in w.seq_names]
+    lens = [model.length(n) for n in w.seq_names]
+    q64 = w.queries().to(torch.float64).numpy()
+    es = {"bf16": 2, "f16": 2, "f32": 4, "fp8": 1}[w.dtype]
+    cache = {}
+
+    def resolve(p):
+        if p[0] not in cache:
+            k, v = w.kv(p[0])
+            cache[p[0]] = (k.to(torch.float64).numpy(), v.to(torch.float64).numpy())
+        kk, vv = cache[p[0]]
+        return kk[p[1]], vv[p[1]]
+
+    elapsed, kv_bytes, done = 0.0, 0, 0
+    with threadpool_limits(limits=1):
+        while elapsed < budget_s:
+            for i in share:
+                for key in set(x[0] for x in _walk_keys(pool, tables[i], lens[i])):
+                    resolve((key, 0))
+                t0 = time.perf_counter()
+                paged_decode(pool, resolve, tables, lens, q64, w.num_kv_heads, w.scale, rows=[i])
+                elapsed += time.perf_counter() - t0
+                cache.clear()
+                w.drop_cache()
+                kv_bytes += lens[i] * w.num_kv_heads * w.head_dim * 2 * es
+                done += 1
+                if elapsed >= budget_s:
+                    break
+    return kv_bytes, elapsed, done
+
+
+def cpu_baseline_all_cores(name: str, num_seqs: int, budget_s: float, max_procs: int = 16):
+    """The same oracle on every host core this process may use (one process per
+    core, capped at the machine's CPU share), sequences dealt round-robin; rate =
+    all processes' KV bytes / the longest process's oracle time."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    cores = len(os.sched_getaffinity(0))
+    procs = max(1, min(cores, max_procs, num_seqs))
+    shares = [list(range(r, num_seqs, procs)) for r in range(procs)]
+    ctx = mp.get_context("spawn")                  # fresh interpreters: no GPU state inherited
+    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in env_keys}
+    for k in env_keys:
+        os.environ[k] = "1"
+    try:
+        # a worker that dies raises here instead of being replaced
+        with ProcessPoolExecutor(max_workers=procs, mp_context=ctx) as ex:
+            res = list(ex.map(_cpu_worker, [(name, sh, budget_s) for sh in shares],
+                              timeout=budget_s * 4 + 300))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    kv = sum(r[0] for r in res)
+    secs = max(r[1] for r in res)
+    done = sum(r[2] for r in res)
+    return {"value": kv / secs / 1e9, "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "sample": f"{done} sequence decodes over {procs} processes (one thread each, "
+                      f"sequences dealt round-robin), about {budget_s:.0f} s of oracle time "
+                      f"per process"}
 
 
 def device_copy_gbs(reps: int = 10) -> float:
@@ -543,7 +636,7 @@ def run(args):
                      "traffic": (_measured_traffic(not args.unfused, ps)
                                  if args.workload == "gqa-bf16-b256" else None),
                      "kernel": ("pa_decode_attention" if args.unfused else "pa_decode_step")
-                     + " (decode_kernel" + (" + reduce_kernel" if ps and ps < int(lens.max())
+                     + " (decode_kernel" + (" + reduce_kernel" if step.workspace.numel() > 1
                                             else "") + ")",
                      "algorithmic_bytes": alg},
     }
@@ -554,6 +647,9 @@ def run(args):
         line["sweep_ms_per_step"] = {str(p): round(v[0], 5) for p, v in results.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(make(), args.cpu_budget)
+        if not args.no_all_core_baseline:
+            line["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(
+                args.workload, w.num_seqs, args.cpu_budget * 2 / 3)
     print(json.dumps(line), flush=True)
 
 
@@ -572,6 +668,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="three launches per step instead of pa_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-all-core-baseline", action="store_true",
+                    help="skip the all-core oracle figure (the one-thread figure still runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run three plain 512 MiB device copies (counter calibration)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,

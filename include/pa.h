@@ -182,9 +182,13 @@ PA_API pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_
 
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode_attention
- * needs for these arguments (0 when partition_size == 0 or when every
- * sequence fits in one partition): one fp32 record per (sequence, KV head,
- * partition) of G*head_dim + 2*G floats rounded up to 128 bytes, G = Hq/Hkv.
+ * needs for these arguments (0 when no split is made: partition_size == 0,
+ * every sequence fits in one partition, or PA_PARTITION_AUTO keeps one
+ * pass): one fp32 record per (sequence, KV head, partition), or per (KV
+ * head, unit) for a planned split, of G*head_dim + 2*G floats rounded up to
+ * 128 bytes, G = Hq/Hkv; a planned split adds two int32 per sequence.
+ * Splitting a sequence's context is not on the pages: the split and its
+ * combine are the ordinary rescaling of partial softmax sums.
  * `bytes` is host memory; num_q_heads must be a multiple of num_kv_heads.
  */
 PA_API pa_status pa_decode_workspace_size(const pa_pool_desc* pool, int32_t num_seqs,
