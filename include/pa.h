@@ -274,6 +274,34 @@ PA_API pa_status pa_decode_step(const pa_pool_desc* pool, void* k_pool, void* v_
                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* Size of the per-GPU device scratch behind pa_decode_step_noalloc. */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pa_decode_step_noalloc -- pa_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * results.  A split's partial records live in a device array of
+ * PA_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU, created
+ * when the library is loaded on that GPU and kept until the process ends;
+ * the call itself allocates nothing.
+ *   Returns PA_ERR_WORKSPACE, enqueueing nothing, when the call's workspace
+ *   (pa_decode_workspace_size with the same arguments) exceeds that size, and
+ *   PA_ERR_HIP when the array's address cannot be looked up on the current
+ *   device.
+ *   Every call on one GPU in a process shares that GPU's array, which keeps
+ *   the last call's contents: calls that may overlap on one GPU (several
+ *   streams or host threads) race and give undefined results; serialise
+ *   them, or use pa_decode_step with separate workspaces.
+ */
+PA_API pa_status pa_decode_step_noalloc(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                                        const void* k_new, const void* v_new, int64_t new_stride,
+                                        const void* q, void* out, pa_dtype out_dtype,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, float scale, int32_t max_context_len,
+                                        int32_t partition_size, void* stream);
+
 /*
  * pa_prefill_attention -- multi-token (prefill or chunked-prefill) attention
  * through the block tables.  Sequence i stores L_i tokens; its chunk is the

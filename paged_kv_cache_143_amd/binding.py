@@ -22,7 +22,9 @@ DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_attention",
-           "pa_decode_step", "pa_prefill_attention", "pa_swap_blocks", "pa_validate_tables")
+           "pa_decode_step", "pa_prefill_attention", "pa_swap_blocks", "pa_validate_tables",
+           "pa_decode_step_noalloc")
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 
 
@@ -87,6 +89,9 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_step.restype = I32
     L.pa_decode_step.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I64, P, P, I32, P, I32,
                                  P, I32, I32, ctypes.c_float, I32, I32, P, ctypes.c_size_t, P]
+    L.pa_decode_step_noalloc.restype = I32
+    L.pa_decode_step_noalloc.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I64, P, P, I32,
+                                         P, I32, P, I32, I32, ctypes.c_float, I32, I32, P]
     L.pa_prefill_attention.restype = I32
     L.pa_prefill_attention.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I32, P, P, I32, P,
                                        I32, I32, ctypes.c_float, I32, I32, P]
@@ -156,6 +161,15 @@ def pa_decode_step(desc, k_pool, v_pool, k_new, v_new, new_stride, q, out, out_d
                                 out, out_dtype, block_tables, max_blocks_per_seq, context_lens,
                                 num_seqs, num_q_heads, scale, max_context_len, partition_size,
                                 workspace, workspace_bytes, stream)
+
+
+def pa_decode_step_noalloc(desc, k_pool, v_pool, k_new, v_new, new_stride, q, out, out_dtype,
+                           block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                           scale, max_context_len, partition_size, stream) -> int:
+    return lib().pa_decode_step_noalloc(ctypes.byref(desc), k_pool, v_pool, k_new, v_new,
+                                        new_stride, q, out, out_dtype, block_tables,
+                                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                        scale, max_context_len, partition_size, stream)
 
 
 def pa_prefill_attention(desc, k_pool, v_pool, q, out, out_dtype, q_start, block_tables,

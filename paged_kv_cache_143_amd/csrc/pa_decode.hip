@@ -40,6 +40,7 @@
 //
 // fp32 pools use v_mfma_f32_16x16x4_f32 in the same roles (one k per lane).
 #include <algorithm>
+#include <mutex>
 
 #include "pa_tile.h"
 
@@ -1206,6 +1207,30 @@ static pa_status decode_impl(const pa_pool_desc* pool, void* k_pool, void* v_poo
   }
 }
 
+// Device scratch of pa_decode_step_noalloc: the split workspace for callers
+// that cannot allocate.  One copy per GPU, created when the library's code
+// object loads there and held until the process ends.  In host code
+// `scratch` names a host-side stand-in: only the per-device address that
+// hipGetSymbolAddress returns may reach a kernel or a copy.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept; null if the lookup fails.
+static void* scratch_on_current_device() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -1250,6 +1275,27 @@ pa_status pa_decode_step(const pa_pool_desc* pool, void* k_pool, void* v_pool, c
   return decode_impl(pool, k_pool, v_pool, k_new, v_new, new_stride, q, out, out_dtype,
                      block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                      scale, max_context_len, partition_size, workspace, workspace_size, stream);
+}
+
+pa_status pa_decode_step_noalloc(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                                 const void* k_new, const void* v_new, int64_t new_stride,
+                                 const void* q, void* out, pa_dtype out_dtype,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, float scale, int32_t max_context_len,
+                                 int32_t partition_size, void* stream) {
+  if (!k_new || !v_new) return PA_ERR_INVALID_ARG;
+  size_t need = 0;
+  const pa_status st = pa_decode_workspace_size(pool, num_seqs, num_q_heads, max_context_len,
+                                                partition_size, &need);
+  if (st != PA_OK) return st;
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = scratch_on_current_device())) return PA_ERR_HIP;
+  return decode_impl(pool, k_pool, v_pool, k_new, v_new, new_stride, q, out, out_dtype,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                     scale, max_context_len, partition_size, ws,
+                     need > 0 ? (size_t)PA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 }  // extern "C"
