@@ -22,14 +22,15 @@
 // NQ groups; the four wavefronts of a workgroup take consecutive row ranges of
 // one (sequence, KV head).
 //
-// 16-bit pools (prefill_ring_kernel): the four wavefronts walk together in
+// 16-bit and FP8 pools (prefill_ring_kernel): the four wavefronts walk together in
 // steps of 32 keys.  Each step's K and V are copied once per workgroup from
-// the pool into a four-stage LDS ring by global-to-LDS loads issued three
-// steps ahead (the loading lanes gather the rows through the block table),
+// the pool into a four-stage LDS ring (FP8: three) by global-to-LDS loads
+// issued ahead (the loading lanes gather the rows through the block table),
 // and every wavefront reads its fragments from LDS, the next step's K while
 // the current step's softmax runs.  Table entries come in
 // windows of 64 blocks, one per lane, and reach the loading lanes by lane
-// permutation.  FP8 and fp32 pools (prefill_kernel): each wavefront walks on
+// permutation; FP8 codes land raw and are widened to the 16-bit layout in LDS
+// once per workgroup.  fp32 pools (prefill_kernel): each wavefront walks on
 // its own, one sub-tile per step with a second buffer one step ahead, through
 // cached buffer loads.  Each XCD runs the row tiles of one (sequence, KV head)
 // after another, last rows (the most keys) first, so its resident workgroups
