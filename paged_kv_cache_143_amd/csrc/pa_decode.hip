@@ -99,7 +99,7 @@ struct DecodeArgs {
 // within that bin in index order (ballots).  About six barriers and
 // O(S / threads + kRankBins / threads) work per thread.
 constexpr int kRankBins = 2048;
-constexpr int kRankLdsInts = kRankBins + kWaves + 3;
+constexpr int kRankLdsInts = kRankBins + kWaves + 4;
 // Up to this many sequences, ranking by pairwise comparison (O(S^2 / threads),
 // two barriers) is cheaper than the counting selection's fixed cost.
 #ifndef PA_PAIRWISE_RANK_MAX
@@ -109,15 +109,15 @@ constexpr int kPairwiseRankMax = PA_PAIRWISE_RANK_MAX;
 
 
 
-// Length of sequence i as attended: clipped to [0, max_len] and to what its
-// table row can address.
-__device__ inline int clip_len(const DecodeArgs& a, int i) {
-  int L = a.lens[i];
+// A stored length as attended: clipped to [0, max_len] and to what a table
+// row can address.
+__device__ inline int clip_stored(const DecodeArgs& a, int L) {
   L = L < 0 ? 0 : L;
   L = L > a.max_len ? a.max_len : L;
   const int64_t cap = (int64_t)a.max_blocks * a.block_size;
   return (int64_t)L > cap ? (int)cap : L;
 }
+__device__ inline int clip_len(const DecodeArgs& a, int i) { return clip_stored(a, a.lens[i]); }
 
 // Lengths are ranked in bins of 2^PA_RANK_SHIFT 16-token tiles (128 tokens),
 // and sequences of one bin keep their batch order: the forks of one request,
@@ -128,14 +128,19 @@ __device__ inline int clip_len(const DecodeArgs& a, int i) {
 #ifndef PA_RANK_SHIFT
 #define PA_RANK_SHIFT 3
 #endif
-__device__ inline int rank_bin(const DecodeArgs& a, int i) {
-  const int L = clip_len(a, i);
+__device__ inline int bin_of_stored(const DecodeArgs& a, int stored) {
+  const int L = clip_stored(a, stored);
   int nb = ((L + kRows - 1) / kRows) >> PA_RANK_SHIFT;   // work measure: 16-token sub-tiles
   nb = nb > kRankBins - 1 ? kRankBins - 1 : nb;
   return kRankBins - 1 - nb;                   // longest first
 }
+__device__ inline int rank_bin(const DecodeArgs& a, int i) { return bin_of_stored(a, a.lens[i]); }
 
-__device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
+// Both rankings return (sequence, its stored length as read while ranking):
+// the unit then needs no second read of the length before its first table
+// load (under a full memory pipeline each dependent read costs microseconds).
+
+__device__ inline int2 seq_of_rank(const DecodeArgs& a, int r, int* lds) {
   static_assert(kRankBins % kThreads == 0, "bins per thread");
   constexpr int kPer = kRankBins / kThreads;
   int* hist = lds;
@@ -149,7 +154,8 @@ __device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
   __syncthreads();
   // Each thread's first sequence's bin, kept for the final pass: one round
   // of length reads per workgroup when S <= kThreads (1 us of the launch).
-  const int my_bin = t < S ? rank_bin(a, t) : -1;
+  const int my_len = t < S ? a.lens[t] : 0;
+  const int my_bin = t < S ? bin_of_stored(a, my_len) : -1;
   if (t < S) atomicAdd(&hist[my_bin], 1);
   for (int i = t + kThreads; i < S; i += kThreads) atomicAdd(&hist[rank_bin(a, i)], 1);
   __syncthreads();
@@ -186,7 +192,8 @@ __device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
   // The `within`-th sequence (by index) of that bin.
   for (int base = 0; base < S; base += kThreads) {
     const int i = base + t;
-    const bool hit = i < S && (base == 0 ? my_bin : rank_bin(a, i)) == bin;
+    const int len_i = base == 0 ? my_len : i < S ? a.lens[i] : 0;
+    const bool hit = i < S && (base == 0 ? my_bin : bin_of_stored(a, len_i)) == bin;
     const unsigned long long m = __ballot(hit);
     if (lane == 0) scratch[w] = __popcll(m);
     __syncthreads();
@@ -197,33 +204,46 @@ __device__ inline int seq_of_rank(const DecodeArgs& a, int r, int* lds) {
     }
     if (within < total) {                      // uniform across the workgroup
       const int mine = wbefore + __popcll(m & ((1ull << lane) - 1ull));
-      if (hit && mine == within) scratch[kWaves + 2] = i;
+      if (hit && mine == within) {
+        scratch[kWaves + 2] = i;
+        scratch[kWaves + 3] = len_i;
+      }
       __syncthreads();
-      const int seq = scratch[kWaves + 2];
+      const int2 found = make_int2(scratch[kWaves + 2], scratch[kWaves + 3]);
       __syncthreads();                         // LDS is reused afterwards
-      return seq;
+      return found;
     }
     within -= total;
     __syncthreads();
   }
-  return 0;                                    // not reached: r < S
+  return make_int2(0, 0);                      // not reached: r < S
 }
 
 // rank(i) = #{j : key_j > key_i} with unique keys (block count, then lower index).
-__device__ inline int seq_of_rank_pairwise(const DecodeArgs& a, int r, int* lds) {
+// LDS: keys [0, S), the result at kPairwiseRankMax and +1, lengths from +2.
+__device__ inline int2 seq_of_rank_pairwise(const DecodeArgs& a, int r, int* lds) {
+  static_assert(2 * kPairwiseRankMax + 2 <= kRankLdsInts, "pairwise ranking's LDS");
   const int S = a.num_seqs;
-  for (int i = threadIdx.x; i < S; i += kThreads) lds[i] = ((kRankBins - 1 - rank_bin(a, i)) << 12) | (4095 - i);
+  int* lens = lds + kPairwiseRankMax + 2;
+  for (int i = threadIdx.x; i < S; i += kThreads) {
+    const int len = a.lens[i];
+    lens[i] = len;
+    lds[i] = ((kRankBins - 1 - bin_of_stored(a, len)) << 12) | (4095 - i);
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < S; i += kThreads) {
     const int ki = lds[i];
     int rank = 0;
     for (int j = 0; j < S; ++j) rank += lds[j] > ki ? 1 : 0;
-    if (rank == r) lds[kPairwiseRankMax] = i;
+    if (rank == r) {
+      lds[kPairwiseRankMax] = i;
+      lds[kPairwiseRankMax + 1] = lens[i];
+    }
   }
   __syncthreads();
-  const int seq = lds[kPairwiseRankMax];
+  const int2 found = make_int2(lds[kPairwiseRankMax], lds[kPairwiseRankMax + 1]);
   __syncthreads();
-  return seq;
+  return found;
 }
 
 // ---- planned split (automatic partitioning) ----
@@ -564,18 +584,11 @@ __device__ inline void load_pair8(Frag<Tag, D, true>& f, uint64_t ka, uint64_t k
     f.v[n] = Cached ? *(g8)(vl + n * 128) : __builtin_nontemporal_load((g8)(vl + n * 128));
 }
 
-// Sharing test for the cache policy: whether a neighbouring row of the batch
-// lists the same physical block at logical index jb (a false match only
-// changes how that unit's tiles are cached).
+// Cache policy for units whose sequence shares its first block with a
+// neighbouring row of the batch (0: stream every unit).
 #ifndef PA_SHARED_CACHED
 #define PA_SHARED_CACHED 1
 #endif
-__device__ inline bool shared_with_neighbour(const DecodeArgs& a, const int32_t* trow, int seq,
-                                             int jb, int phys) {
-  if (!PA_SHARED_CACHED) return false;
-  return (seq > 0 && trow[jb - a.max_blocks] == phys) ||
-         (seq + 1 < a.num_seqs && trow[jb + a.max_blocks] == phys);
-}
 
 // Register buffers in the block ring (one block ahead of the one being
 // computed); FP8 runs more wavefronts per SIMD instead of a deeper ring.
@@ -618,13 +631,18 @@ void decode_kernel(DecodeArgs a) {
       *reinterpret_cast<int2*>(a.plan_hdr + 2 * pu.seq) = make_int2(pu.first, pu.count);
   };
   const int part = a.planned ? pu.part : rest / a.num_seqs;
-  const int seq = a.planned ? pu.seq
-                  : !a.longest_first ? rest % a.num_seqs
-                  : a.num_seqs <= kPairwiseRankMax
-                      ? seq_of_rank_pairwise(a, rest % a.num_seqs, reinterpret_cast<int*>(smem))
-                      : seq_of_rank(a, rest % a.num_seqs, reinterpret_cast<int*>(smem));
+  // (sequence, stored length or -1 when not read yet); both are uniform.
+  int2 sr = make_int2(a.planned ? pu.seq : rest % a.num_seqs, -1);
+  if (!a.planned && a.longest_first)
+    sr = a.num_seqs <= kPairwiseRankMax
+             ? seq_of_rank_pairwise(a, rest % a.num_seqs, reinterpret_cast<int*>(smem))
+             : seq_of_rank(a, rest % a.num_seqs, reinterpret_cast<int*>(smem));
+  const int seq = __builtin_amdgcn_readfirstlane(sr.x);
+  const int stored = sr.y >= 0 ? __builtin_amdgcn_readfirstlane(sr.y)
+                     : a.planned && a.k_new == nullptr ? 0
+                                                       : a.lens[seq];
 
-  const int L = a.planned ? pu.len : clip_len(a, seq);
+  const int L = a.planned ? pu.len : clip_stored(a, stored);
   const int n_parts = a.planned ? pu.count : (L + a.ps - 1) / a.ps;
   const int G = a.group;
   const int head0 = g * G;
@@ -635,7 +653,7 @@ void decode_kernel(DecodeArgs a) {
   // table row reaches it -- also when that position lies beyond the attended
   // length L (a length clipped to max_len).  It joins the attention only when
   // it is attended, i.e. when the length was not clipped.
-  const int raw_len = a.k_new != nullptr ? a.lens[seq] : 0;
+  const int raw_len = a.k_new != nullptr ? stored : 0;
   const bool store_new = raw_len >= 1 && (raw_len - 1) / a.block_size < a.max_blocks;
   const bool patch_new = store_new && raw_len == L;
   NewToken<Tag, D> tok;
@@ -712,7 +730,7 @@ void decode_kernel(DecodeArgs a) {
   // which is patched first).  A block is then a lane broadcast, not address
   // arithmetic.  Blocks past the wavefront's last one (the ring's prefetch)
   // get count 0 and a size-0 resource: no memory access, static wait counts
-  // (P8 tiles read block 0's tile of the head instead, see open_chunk).
+  // (P8 tiles read block 0's tile of the head instead, see open_table).
   const uint64_t k_base = (uint64_t)a.k_pool;
   const uint64_t v_delta = (uint64_t)a.v_pool - k_base;
   const int sub_shift = a.sub >> 1;          // sub-tiles per block: 1 or 2
@@ -756,8 +774,19 @@ void decode_kernel(DecodeArgs a) {
       attend_regs(fr, nvr);
     }
   };
-  auto open_chunk = [&](auto cached_c) {
+  // The chunk's table entries and tile descriptors (no tile loads).
+  int t_a = -1, t_b = -1;                      // this lane's table entries (P8: two)
+  auto read_table = [&]() {
     n = min(kWave, cnt - c0);
+    const int j = first + c0 + lane;
+    if constexpr (P8) {
+      t_a = lane < n ? trow[2 * j] : -1;
+      t_b = lane < n && (2 * j + 1) * 8 < L ? trow[2 * j + 1] : -1;
+    } else {
+      t_a = lane < n ? trow[j >> sub_shift] : -1;
+    }
+  };
+  auto open_table = [&]() {
     const int j = first + c0 + lane;
     if constexpr (P8) {
       // Blocks 2j and 2j+1.  Decode has no causal order, so valid blocks are
@@ -766,9 +795,7 @@ void decode_kernel(DecodeArgs a) {
       // the wavefront's last (the ring's prefetch), read block 0's tile of
       // this head (in bounds; shared by every such read, so it stays cached)
       // and are masked by the count.
-      const int pa_ = lane < n ? trow[2 * j] : -1;
-      const bool has_b = lane < n && (2 * j + 1) * 8 < L;
-      const int pb_ = has_b ? trow[2 * j + 1] : -1;
+      const int pa_ = t_a, pb_ = t_b;
       const bool oka = pa_ >= 0 && pa_ < a.num_blocks;
       const bool okb = pb_ >= 0 && pb_ < a.num_blocks;
       const int ca = oka ? min(8, L - 16 * j) : 0;
@@ -786,7 +813,7 @@ void decode_kernel(DecodeArgs a) {
       d_lo2 = (uint32_t)ab;
       d_hi2 = (uint32_t)(ab >> 32);
     } else {
-      const int phys = lane < n ? trow[j >> sub_shift] : -1;
+      const int phys = t_a;
       const bool ok = phys >= 0 && phys < a.num_blocks;
       int c = ok ? min(a.rows, L - j * a.rows) : 0;
       if (own_patch && j == j_new) c = -c;
@@ -796,6 +823,9 @@ void decode_kernel(DecodeArgs a) {
       d_lo = (uint32_t)addr;
       d_hi = (uint32_t)(addr >> 32);
     }
+  };
+  // The ring's first NBuf - 1 tiles of the chunk.
+  auto prefetch = [&](auto cached_c) {
 #pragma unroll
     for (int u = 0; u + 1 < NBuf; ++u) load_into(cached_c, f[u], u, nv[u]);
   };
@@ -803,7 +833,10 @@ void decode_kernel(DecodeArgs a) {
   // The block loop, compiled for each cache policy (one policy per unit keeps
   // the loads unconditional and their wait counts static).
   auto block_loop = [&](auto cached_c) {
-    if (cnt > 0) open_chunk(cached_c);
+    if (cnt > 0) {
+      open_table();
+      prefetch(cached_c);
+    }
     if (own_patch) {                            // every wavefront reaches this barrier
       tok.stage(stage);
       __syncthreads();
@@ -816,7 +849,11 @@ void decode_kernel(DecodeArgs a) {
   // compile-time constant in the unrolled body (registers are never indexed at
   // run time).
     for (; c0 < cnt; c0 += kWave) {
-      if (c0 > 0) open_chunk(cached_c);
+      if (c0 > 0) {
+        read_table();
+        open_table();
+        prefetch(cached_c);
+      }
       for (int i = 0; i < n; i += NBuf) {
 #pragma unroll
         for (int u = 0; u < NBuf; ++u) {
@@ -828,13 +865,28 @@ void decode_kernel(DecodeArgs a) {
       }
     }
   };
+  // The first chunk's table entries and the sharing test below read in one
+  // memory round trip with the q and current-token loads above.
+  if (cnt > 0) read_table();
   // A sequence whose first block the neighbouring row of the batch also
   // lists (forks of one prompt, placed side by side) reads its tiles through
   // the caches, so the forks' units share the prompt's tiles in L2; any other
-  // sequence streams its tiles, which are read once per call.  FP8 pools keep
-  // one (streaming) loop: the second copy measured 2-3 % slower there.
-  const bool cached_unit =
-      !IsFP8<Tag>::value && L > 0 && shared_with_neighbour(a, trow, seq, 0, trow[0]);
+  // sequence streams its tiles, which are read once per call (a false match
+  // would only change how a unit's tiles are cached).  The three entries are
+  // read unconditionally (in-bounds indexes) so the reads go out together.
+  // FP8 pools keep one (streaming) loop: the second copy measured 2-3 %
+  // slower there.
+  bool cached_unit = false;
+  if constexpr (!IsFP8<Tag>::value) {
+    if (PA_SHARED_CACHED) {
+      const int mb = a.max_blocks;
+      const bool has_prev = seq > 0, has_next = seq + 1 < a.num_seqs;
+      const int32_t b0 = trow[0];                // L > 0 here, so the row has an entry
+      const int32_t bp = trow[has_prev ? -mb : 0];
+      const int32_t bn = trow[has_next ? mb : 0];
+      cached_unit = (has_prev & (bp == b0)) | (has_next & (bn == b0));
+    }
+  }
   if constexpr (IsFP8<Tag>::value) {
     block_loop(std::false_type());
   } else {

@@ -264,17 +264,22 @@ constexpr float kRescaleLog2 = 8.f;
 // back to 0 so that -inf - -inf never occurs.  `qk()` returns the scores,
 // lane (h + 16q) holding tokens 4q..4q+3 of head h; `pv(p, t0)` adds
 // V^T P for this lane's four probabilities p of tokens t0 .. t0 + 3.
-template <int D, class QK, class PV>
+template <int D, bool SkipWhole = false, class QK, class PV>
 __device__ inline void attend_core(QK qk, PV pv, State<D>& st, int n_valid, float qk_scale,
                                    int lane, int lim) {
   f32x4 s = qk();
   const int t0 = 4 * (lane >> 4);
+  // select, never multiply: tails may hold NaN.  `lim` (per lane: its
+  // column's last visible row + 1) is the causal limit of multi-token queries.
+  // With SkipWhole, a sub-tile with every row stored and no causal limit
+  // (nearly every one in decode) skips the selects behind a uniform branch;
+  // the 16-bit kernels keep the unconditional form (the branch costs them
+  // registers they do not have).
+  const bool masked = !SkipWhole || n_valid < kRows || lim < kRows;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     s[r] *= qk_scale;
-    // select, never multiply: tails may hold NaN.  `lim` (per lane: its
-    // column's last visible row + 1) is the causal limit of multi-token queries.
-    if (t0 + r >= n_valid || t0 + r >= lim) s[r] = -INFINITY;
+    if (masked && (t0 + r >= n_valid || t0 + r >= lim)) s[r] = -INFINITY;
   }
   // Online softmax with a lazily moved base: only when some score of the
   // wavefront exceeds its column's base by more than kRescaleLog2 (always on
@@ -307,7 +312,7 @@ __device__ inline void attend_core(QK qk, PV pv, State<D>& st, int n_valid, floa
 // acc[d][h] += V^T P with P split into a high and a low part placed in the two
 // k halves against a duplicated V fragment.  Tail tokens of V are zeroed
 // (their P is zero, but 0 * NaN is NaN).
-template <class Tag, int D, class KF, class VF>
+template <class Tag, int D, bool SkipWhole = false, class KF, class VF>
 __device__ inline void attend16(KF kf, VF vf, const QFrag<Tag, D>& qf, State<D>& st, int n_valid,
                                 float qk_scale, int lane, int lim = kRows) {
   auto qk = [&]() {
@@ -338,7 +343,7 @@ __device__ inline void attend16(KF kf, VF vf, const QFrag<Tag, D>& qf, State<D>&
       st.acc[n] = mma32<Tag>(va, pb, st.acc[n]);
     }
   };
-  attend_core<D>(qk, pv, st, n_valid, qk_scale, lane, lim);
+  attend_core<D, SkipWhole>(qk, pv, st, n_valid, qk_scale, lane, lim);
 }
 
 template <class Tag, int D>
@@ -379,7 +384,7 @@ __device__ inline void attend_block(const Frag<Tag, D>& f, const QFrag<Tag, D>& 
 template <int D>
 __device__ inline void attend_block_fp8(const Frag<TagFP8, D>& f, const QFrag<TagFP8, D>& qf,
                                         State<D>& st, int n_valid, float qk_scale, int lane) {
-  attend16<TagBF16, D>(
+  attend16<TagBF16, D, true>(
       [&](int m) {
         return u32x4{fp8x2_to_bf16x2<false>(f.k[m][0]), fp8x2_to_bf16x2<true>(f.k[m][0]),
                      fp8x2_to_bf16x2<false>(f.k[m][1]), fp8x2_to_bf16x2<true>(f.k[m][1])};
