@@ -6,8 +6,9 @@ several tiles and ragged tails, every GQA group size up to 16, head_dim 64
 and 128, NaN poison in unused slots and free blocks, padded table entries,
 recycled blocks with stale tenants, split-context partitions, forks sharing
 blocks before and after copy-on-write, zero-length rows, lengths clipped by
-max_context_len in the fused step, and every full-size workload (every row of
-the batch against the oracle) in the launch configuration the benchmark
+max_context_len in the fused step, batches of up to 700 sequences with tied
+lengths under longest-first dispatch, and every full-size workload (every row
+of the batch against the oracle) in the launch configuration the benchmark
 times.  Outputs start as NaN, so a row that no kernel writes fails.
 """
 import numpy as np
@@ -242,6 +243,40 @@ def _poison_current_tokens(batch):
     shape = (len(slots), w.num_kv_heads, w.head_dim)
     nan = torch.full(shape, float("nan"), dtype=W.DTYPES[w.input_dtype], device="cuda")
     batch.kv.write(nan, nan, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+
+
+def _tied(name, seed, values, n, dtype="bf16"):
+    """n sequences whose lengths are drawn from a few values (ties in the
+    ranking's length bins)."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.choice(values, n)]
+    return W.independent(name, seed, dtype, lengths, 4, 2, 64, W._pool_for(lengths, 16, 0.1))
+
+
+# Longest-first dispatch ranks the sequences in every workgroup: pairwise up
+# to 128 sequences, by counting above (several passes over the lengths once
+# there are more sequences than a workgroup has threads).  Every row of each
+# batch is checked, so a rank that is not a bijection (a row never written,
+# or written twice) fails.
+RANKED = {
+    "100seqs-tied-pairwise": lambda: _tied("rk-pw", 94, [33, 34, 200], 100),
+    "300seqs-one-bin": lambda: _tied("rk-one", 93, [100, 101, 127], 300),
+    "600seqs-U1..300": lambda: W.scaled("rk600", 91, 600, 1, 300, 4, 2, 64, "bf16"),
+    "700seqs-tied-bins-f16": lambda: _tied("rk-tie", 92, [17, 160, 161, 300], 700, "f16"),
+}
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name", list(RANKED))
+def test_longest_first_ranking_covers_every_row(name, fused):
+    w = RANKED[name]()
+    batch = build_batch(w, drop_payload_cache=False)
+    got = DecodeStep(batch, partition_size=0, fused=fused)().float().cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, full_decode(w))
+    announce(f"{name} fused={fused}: all {w.num_seqs} rows max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
 
 
 FUSED = {
