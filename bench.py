@@ -113,13 +113,16 @@ def kernel_source_digest() -> str:
 
 def _measured_traffic(workload: str, fused: bool, partition: int):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    record of this workload, only while the kernel sources are the ones it was
-    taken on (and for the configuration it was taken in); otherwise None."""
+    record of this workload (a split launch: the decode and combine kernels
+    together), only while the kernel sources are the ones it was taken on and
+    for the configuration it was taken in (fused step, same partition
+    setting); otherwise None."""
     try:
         rec = json.load(open(COUNTERS.format(workload.replace("-", "_"))))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_digest() or not fused or partition != 0:
+    if (rec.get("kernel_source_sha256") != kernel_source_digest() or not fused
+            or partition != rec.get("partition_size", 0)):
         return None
     return rec.get("traffic_bytes_per_launch")
 
