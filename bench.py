@@ -647,6 +647,12 @@ def run(args):
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.num_seqs / (ms_step / 1e3), 1),
         "context_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
+        # decode tokens per second over the KV-reading launch alone (attention
+        # only when the write runs separately)
+        ("attention_only_tokens_per_s" if args.unfused else "kv_launch_tokens_per_s"):
+            round(w.num_seqs / (float(np.median(dec_ms)) / 1e3), 1),
+        # q.k and P.V: 4 d flops per (context token, query head), plus one exp each
+        "algorithmic_gflop": round(float(lens.sum()) * w.num_q_heads * 4 * w.head_dim / 1e9, 4),
         "kernels_us": {"separate_write_and_slots_median":
                            round(float(np.median(write_ms)) * 1e3, 2) if args.unfused else 0.0,
                        "kv_launch_median": round(float(np.median(dec_ms)) * 1e3, 2),
