@@ -7,9 +7,10 @@ and 128, NaN poison in unused slots and free blocks, padded table entries,
 recycled blocks with stale tenants, split-context partitions, forks sharing
 blocks before and after copy-on-write, zero-length rows, lengths clipped by
 max_context_len in the fused step, batches of up to 700 sequences with tied
-lengths under longest-first dispatch, and every full-size workload (every row
-of the batch against the oracle) in the launch configuration the benchmark
-times.  Outputs start as NaN, so a row that no kernel writes fails.
+lengths under longest-first dispatch, maximum sizes (4096 sequences; one
+65,536-token sequence in 1024 partitions), and every full-size workload
+(every row of the batch against the oracle) in the launch configuration the
+benchmark times.  Outputs start as NaN, so a row that no kernel writes fails.
 """
 import numpy as np
 import pytest
@@ -276,6 +277,33 @@ def test_longest_first_ranking_covers_every_row(name, fused):
     assert np.isfinite(got).all()
     err = row_rel_err(got, full_decode(w))
     announce(f"{name} fused={fused}: all {w.num_seqs} rows max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
+
+
+# Maximum sizes: 4096 sequences (32768 workgroups; the counting ranking makes
+# 16 passes over the lengths), and one 65,536-token sequence split by the
+# library's plan or into 1024 partitions of 64 tokens per row.
+@pytest.mark.parametrize("fused", [True, False])
+def test_4096_sequences_every_row(fused):
+    w = W.scaled("max-s", 401, 4096, 1, 64, 8, 2, 64, "bf16")
+    batch = build_batch(w, drop_payload_cache=False)
+    got = DecodeStep(batch, partition_size=0, fused=fused)().float().cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, full_decode(w))
+    announce(f"4096 sequences fused={fused}: max row rel err {err:.3e}")
+    assert err <= tol_for(w.dtype)
+
+
+@pytest.mark.parametrize("ps", [B.PA_PARTITION_AUTO, 64])
+def test_one_64k_token_sequence(ps):
+    w = W.independent("max-l", 402, "bf16", [65536], 32, 8, 128, 65536 // 16 + 20)
+    batch = build_batch(w, drop_payload_cache=False)
+    got = DecodeStep(batch, partition_size=ps)().float().cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, full_decode(w))
+    announce(f"65536 tokens ps={ps}: max row rel err {err:.3e}")
     assert err <= tol_for(w.dtype)
 
 
