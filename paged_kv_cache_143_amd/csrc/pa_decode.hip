@@ -631,7 +631,9 @@ void decode_kernel(DecodeArgs a) {
       *reinterpret_cast<int2*>(a.plan_hdr + 2 * pu.seq) = make_int2(pu.first, pu.count);
   };
   const int part = a.planned ? pu.part : rest / a.num_seqs;
-  // (sequence, stored length or -1 when not read yet); both are uniform.
+  // (sequence, stored length), both uniform; a negative length field means
+  // the length was not read by a ranking (or is itself negative, which
+  // clips to 0) and is read here.
   int2 sr = make_int2(a.planned ? pu.seq : rest % a.num_seqs, -1);
   if (!a.planned && a.longest_first)
     sr = a.num_seqs <= kPairwiseRankMax
