@@ -153,7 +153,8 @@ __device__ inline int2 seq_of_rank(const DecodeArgs& a, int r, int* lds) {
   for (int b = 0; b < kPer; ++b) hist[t * kPer + b] = 0;
   __syncthreads();
   // Each thread's first sequence's bin, kept for the final pass: one round
-  // of length reads per workgroup when S <= kThreads (1 us of the launch).
+  // of length reads per workgroup when S <= kThreads (about 1 us at the start
+  // of a launch, several under a full memory pipeline).
   const int my_len = t < S ? a.lens[t] : 0;
   const int my_bin = t < S ? bin_of_stored(a, my_len) : -1;
   if (t < S) atomicAdd(&hist[my_bin], 1);
