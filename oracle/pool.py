@@ -87,3 +87,29 @@ class SlotPool:
                     K[i, o] = k
                     V[i, o] = v
         return K, V
+
+
+def copy_batch_violations(pairs: Sequence[Tuple[int, int]], num_blocks: int) -> int:
+    """Pairs of one batched block copy that break the batch's contract.
+
+    Source: "Inside vLLM and TGI", section "Exact CPU block manager and
+    copy-on-write" -- a copy-on-write fills a block just taken from the free
+    list (never shared, never read in the same step) with the contents of the
+    old block -- and transcript paragraph 4.  A batch of such copies issued
+    at once has the meaning of the copies applied one after another only when
+    no block is written twice and no written block is read: every destination
+    distinct, and no destination also a source (its own pair's included).
+
+    A pair with an id outside [0, num_blocks) is skipped by the copy and is
+    not counted, nor does it take part in the checks of other pairs.  Among the
+    remaining pairs, pair i counts once when its destination is the
+    destination of another remaining pair, or the source of any remaining pair.
+    """
+    live = [(int(s), int(d)) for s, d in pairs
+            if 0 <= int(s) < num_blocks and 0 <= int(d) < num_blocks]
+    bad = 0
+    for i, (_, di) in enumerate(live):
+        dup = any(dj == di for j, (_, dj) in enumerate(live) if j != i)
+        read = any(sj == di for sj, _ in live)
+        bad += 1 if (dup or read) else 0
+    return bad

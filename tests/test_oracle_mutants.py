@@ -16,6 +16,7 @@ import oracle.prefill as OPF
 from tests import test_oracle_allocator as TAL
 from tests import test_oracle_attention as TAT
 from tests import test_oracle_paging as TPG
+from tests import test_oracle_pool as TPO
 from tests import test_oracle_prefill as TPF
 from tests import test_oracle_swap as TSW
 from tests import test_oracle_fp8 as TF8
@@ -63,6 +64,16 @@ def _fp8_pins():
 def _pool_pins():
     TAL.test_block_copy_carries_every_slot_including_the_last()
     TAL.test_random_scripts_read_equals_script_contents()
+
+
+def _copy_batch_pins():
+    for pairs, want in [([], 0), ([(1, 2), (3, 4)], 0), ([(1, 2), (3, 2)], 2), ([(1, 2), (2, 3)], 1),
+                        ([(2, 3), (1, 2)], 1), ([(5, 5)], 1), ([(1, 2), (3, 4), (4, 1)], 2),
+                        ([(1, 2), (1, 3), (1, 4)], 0), ([(1, 10), (10, 2), (-1, 3), (2, 4)], 0),
+                        ([(1, 10), (4, 2), (2, 5)], 1), ([(7, -1), (3, 7)], 0)]:
+        TPO.test_hand_worked_batches(pairs, want)
+    TPO.test_valid_batches_are_order_independent()
+    TPO.test_each_violation_kind_can_change_the_result()
 
 
 def _allocator_pins():
@@ -304,6 +315,41 @@ def _pool_copy_filled_prefix_only(self, src, dst):
         self.slots[dst * b + o] = self.slots[src * b + o]
 
 
+def _copy_batch_dups_only(pairs, num_blocks):
+    live = [(s, d) for s, d in pairs if 0 <= s < num_blocks and 0 <= d < num_blocks]
+    return sum(1 for i, (_, di) in enumerate(live)
+               if any(dj == di for j, (_, dj) in enumerate(live) if j != i))
+
+
+def _copy_batch_counts_conflicts(pairs, num_blocks):
+    live = [(s, d) for s, d in pairs if 0 <= s < num_blocks and 0 <= d < num_blocks]
+    n = 0
+    for i, (si, di) in enumerate(live):
+        for j, (sj, dj) in enumerate(live):
+            if j > i and (di == dj or di == sj or dj == si):
+                n += 1
+        n += 1 if si == di else 0
+    return n
+
+
+def _copy_batch_no_skip(pairs, num_blocks):
+    bad = 0
+    for i, (_, di) in enumerate(pairs):
+        dup = any(dj == di for j, (_, dj) in enumerate(pairs) if j != i)
+        bad += 1 if (dup or any(sj == di for sj, _ in pairs)) else 0
+    return bad
+
+
+def _copy_batch_self_allowed(pairs, num_blocks):
+    live = [(s, d) for s, d in pairs if 0 <= s < num_blocks and 0 <= d < num_blocks]
+    bad = 0
+    for i, (_, di) in enumerate(live):
+        dup = any(dj == di for j, (_, dj) in enumerate(live) if j != i)
+        read = any(sj == di for j, (sj, _) in enumerate(live) if j != i)
+        bad += 1 if (dup or read) else 0
+    return bad
+
+
 MUTANTS = [
     ("softmax drops the scale", OA, "softmax_attention", _softmax_no_scale, _attention_pins),
     ("K and V swapped", OA, "softmax_attention", _softmax_kv_swapped, _attention_pins),
@@ -330,6 +376,10 @@ MUTANTS = [
     ("fp8 store multiplies by the scale", OF8, "quantize", _fp8_quantize_multiplies_by_scale, _fp8_pins),
     ("block copy drops each block's last slot", OPL.SlotPool, "copy", _pool_copy_drops_last_slot, _pool_pins),
     ("block copy stops at the first unwritten slot", OPL.SlotPool, "copy", _pool_copy_filled_prefix_only, _pool_pins),
+    ("copy batch: destinations that are read not counted", OPL, "copy_batch_violations", _copy_batch_dups_only, _copy_batch_pins),
+    ("copy batch: conflicts counted instead of pairs", OPL, "copy_batch_violations", _copy_batch_counts_conflicts, _copy_batch_pins),
+    ("copy batch: out-of-pool pairs not skipped", OPL, "copy_batch_violations", _copy_batch_no_skip, _copy_batch_pins),
+    ("copy batch: a block copied onto itself allowed", OPL, "copy_batch_violations", _copy_batch_self_allowed, _copy_batch_pins),
     ("causal mask excludes the row's own position", OPF, "causal_chunk", _chunk_excludes_own_position, _prefill_pins),
     ("chunk positions counted from the chunk start", OPF, "causal_chunk", _chunk_positions_from_chunk_start, _prefill_pins),
     ("causal mask lets a row see the next position", OPF, "causal_chunk", _chunk_sees_next_position, _prefill_pins),
