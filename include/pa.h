@@ -381,6 +381,25 @@ PA_API pa_status pa_validate_tables(const pa_pool_desc* pool, const int32_t* blo
                              int32_t num_seqs, int32_t max_context_len, int32_t* bad_count,
                              void* stream);
 
+/*
+ * pa_validate_copy_pairs -- debug check of one pa_copy_blocks batch against
+ * its contract.  A copy-on-write fills a block just taken from the free list
+ * with the old block's contents ("Inside vLLM and TGI", section "Exact CPU
+ * block manager and copy-on-write"; transcript paragraph 4), so a batch of
+ * copies issued at once means the same as the copies one after another only
+ * when every destination is distinct and none is also a source.  Counts the
+ * pairs that break this: pair i counts once when its destination is the
+ * destination of another pair or the source of any pair (its own included).
+ * Pairs with an id outside [0, num_blocks) are skipped by pa_copy_blocks and
+ * take no part.
+ *   block_pairs  device int32 [n_pairs][2] = {src, dst}
+ *   bad_count    device int32 [1] (output): number of offending pairs
+ * n_pairs^2 comparisons on the device (meant for debug batches).
+ * Asynchronous like every other call; read bad_count after the stream passes.
+ */
+PA_API pa_status pa_validate_copy_pairs(const pa_pool_desc* pool, const int32_t* block_pairs,
+                                        int32_t n_pairs, int32_t* bad_count, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3
 EXPORTS = ("pa_status_string", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_attention",
            "pa_decode_step", "pa_prefill_attention", "pa_swap_blocks", "pa_validate_tables",
-           "pa_decode_step_noalloc")
+           "pa_decode_step_noalloc", "pa_validate_copy_pairs")
 PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 
@@ -99,6 +99,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_swap_blocks.argtypes = [ctypes.POINTER(PoolDesc), P, P, P, P, I32, P, I32, I32, P]
     L.pa_validate_tables.restype = I32
     L.pa_validate_tables.argtypes = [ctypes.POINTER(PoolDesc), P, I32, P, I32, I32, P, P]
+    L.pa_validate_copy_pairs.restype = I32
+    L.pa_validate_copy_pairs.argtypes = [ctypes.POINTER(PoolDesc), P, I32, P, P]
     return L
 
 
@@ -191,6 +193,10 @@ def pa_validate_tables(desc, block_tables, max_blocks_per_seq, context_lens, num
                        max_context_len, bad_count, stream) -> int:
     return lib().pa_validate_tables(ctypes.byref(desc), block_tables, max_blocks_per_seq,
                                     context_lens, num_seqs, max_context_len, bad_count, stream)
+
+
+def pa_validate_copy_pairs(desc, block_pairs, n_pairs, bad_count, stream) -> int:
+    return lib().pa_validate_copy_pairs(ctypes.byref(desc), block_pairs, n_pairs, bad_count, stream)
 
 
 # ---- torch-tensor helpers ------------------------------------------------------
@@ -327,6 +333,15 @@ def swap_blocks_t(desc, k_pool, v_pool, host_k, host_v, host_num_blocks, pairs,
            pa_swap_blocks(desc, _ptr(k_pool), _ptr(v_pool), host_k.data_ptr(), host_v.data_ptr(),
                           int(host_num_blocks), _ptr(pairs), pairs.shape[0], int(direction),
                           _stream()))
+
+
+def validate_copy_pairs_t(desc, pairs, bad_count) -> None:
+    _dev_i32(pairs, "pairs")
+    _dev_i32(bad_count, "bad_count")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n][2]")
+    _check("pa_validate_copy_pairs", pa_validate_copy_pairs(desc, _ptr(pairs), pairs.shape[0],
+                                                             _ptr(bad_count), _stream()))
 
 
 def validate_tables_t(desc, block_tables, context_lens, max_context_len, bad_count) -> None:

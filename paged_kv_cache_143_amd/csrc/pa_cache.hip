@@ -416,6 +416,39 @@ __global__ void validate_kernel(const int32_t* __restrict__ tables, int32_t max_
   if (local) atomicAdd(bad, local);
 }
 
+// Debug check of one batch of block copies: pair i counts once when its
+// destination is the destination of another pair or the source of any pair
+// (its own included).  Pairs with an id outside the pool are skipped by the
+// copy and take no part.  Each workgroup walks all pairs in chunks of its
+// size staged in LDS: n^2 comparisons in all, meant for debug batches.
+__global__ void validate_pairs_kernel(const int32_t* __restrict__ pairs, int32_t n,
+                                      int32_t num_blocks, int32_t* bad) {
+  __shared__ int2 chunk[256];
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  auto in_pool = [&](int2 p) {
+    return p.x >= 0 && p.x < num_blocks && p.y >= 0 && p.y < num_blocks;
+  };
+  const int2 me = i < n ? make_int2(pairs[2 * i], pairs[2 * i + 1]) : make_int2(-1, -1);
+  const bool live = i < n && in_pool(me);
+  bool hit = false;
+  for (int64_t base = 0; base < n; base += blockDim.x) {
+    const int64_t j = base + threadIdx.x;
+    const int2 p = j < n ? make_int2(pairs[2 * j], pairs[2 * j + 1]) : make_int2(-1, -1);
+    chunk[threadIdx.x] = j < n && in_pool(p) ? p : make_int2(-1, -1);
+    __syncthreads();
+    const int m = (int)min((int64_t)blockDim.x, (int64_t)n - base);
+    if (live) {
+      for (int k = 0; k < m; ++k) {
+        const int2 q = chunk[k];
+        if (q.x < 0) continue;                   // a skipped pair
+        hit |= q.x == me.y || (base + k != i && q.y == me.y);
+      }
+    }
+    __syncthreads();
+  }
+  if (hit) atomicAdd(bad, 1);
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -544,6 +577,18 @@ pa_status pa_swap_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool, v
       out ? (const char*)k_pool : hk, out ? (const char*)v_pool : hv, out ? hk : (char*)k_pool,
       out ? hv : (char*)v_pool, block_pairs, n_pairs, block_vecs, (int32_t)segs,
       out ? pool->num_blocks : host_num_blocks, out ? host_num_blocks : pool->num_blocks);
+  return launch_status();
+}
+
+pa_status pa_validate_copy_pairs(const pa_pool_desc* pool, const int32_t* block_pairs,
+                                 int32_t n_pairs, int32_t* bad_count, void* stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (n_pairs < 0 || !bad_count || (n_pairs > 0 && !block_pairs)) return PA_ERR_INVALID_ARG;
+  zero_int_kernel<<<1, 1, 0, (hipStream_t)stream>>>(bad_count);
+  if (n_pairs > 0)
+    validate_pairs_kernel<<<(unsigned)(((int64_t)n_pairs + 255) / 256), 256, 0,
+                            (hipStream_t)stream>>>(block_pairs, n_pairs, pool->num_blocks, bad_count);
   return launch_status();
 }
 

@@ -152,6 +152,9 @@ def test_validate_argument_checks():
     d = _desc()
     assert B.pa_validate_tables(d, 16, 4, 16, 2, 64, 0, 0) == B.PA_ERR_INVALID_ARG
     assert B.pa_validate_tables(d, 16, 4, 0, 2, 64, 16, 0) == B.PA_ERR_INVALID_ARG
+    assert B.pa_validate_copy_pairs(d, 16, 3, 0, 0) == B.PA_ERR_INVALID_ARG      # no count
+    assert B.pa_validate_copy_pairs(d, 0, 3, 16, 0) == B.PA_ERR_INVALID_ARG      # no pairs
+    assert B.pa_validate_copy_pairs(d, 16, -1, 16, 0) == B.PA_ERR_INVALID_ARG    # negative n
 
 
 def test_prefill_argument_checks():

@@ -1,13 +1,14 @@
 """GPU parity of the cache-side entry points against the oracle, bit-exact:
 pa_slot_mapping (slots), pa_write_kv (the whole pool, including never-written
-poison), pa_copy_blocks (copy-on-write forks), pa_validate_tables (counts)."""
+poison), pa_copy_blocks (copy-on-write forks), pa_validate_tables and
+pa_validate_copy_pairs (counts)."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import paging
 from oracle.allocator import run_script
-from oracle.pool import SlotPool
+from oracle.pool import SlotPool, copy_batch_violations
 from paged_kv_cache_143_amd import binding as B
 from paged_kv_cache_143_amd import workloads as W
 from paged_kv_cache_143_amd.paged_cache import PagedKV, build_batch
@@ -179,6 +180,37 @@ def test_copy_blocks_direct_and_skips():
     got_k, got_v = pool_logical(batch.kv, w.num_kv_heads, w.head_dim)
     assert_pool_equal(got_k, want_k)
     assert_pool_equal(got_v, want_v)
+
+
+@pytest.mark.parametrize("n,seed", [(0, 1), (1, 2), (7, 3), (300, 4), (3000, 5)])
+def test_validate_copy_pairs_counts(n, seed):
+    """Random batches with planted duplicate destinations, destinations that
+    are read, self copies and out-of-pool ids, against the oracle's count;
+    several chunks of the kernel's LDS staging when n > 256."""
+    nb = max(8, 3 * n)
+    rng = np.random.default_rng(seed)
+    src = rng.integers(0, nb, n)
+    dst = rng.permutation(nb)[:n] if n <= nb else rng.integers(0, nb, n)
+    pairs = np.stack([src, dst], axis=1).astype(np.int32)
+    for k in range(0, n, 11):                      # plant each kind of violation
+        kind = (k // 11) % 4
+        if kind == 0 and n > 1:
+            pairs[k, 1] = pairs[(k + 1) % n, 1]      # a destination written twice
+        elif kind == 1 and n > 1:
+            pairs[k, 1] = pairs[(k + 3) % n, 0]      # a destination that is read
+        elif kind == 2:
+            pairs[k] = [pairs[k, 0], pairs[k, 0]]    # a block copied onto itself
+        else:
+            pairs[k, rng.integers(0, 2)] = (nb + 5) if rng.random() < 0.5 else -1   # skipped
+    want = copy_batch_violations([tuple(map(int, p)) for p in pairs], nb)
+    desc = B.make_desc(nb, 2, 64, "bf16")
+    bad = torch.full((1,), 777, dtype=torch.int32, device="cuda")
+    B.validate_copy_pairs_t(desc, torch.from_numpy(pairs).cuda().reshape(n, 2), bad)
+    got = int(bad.item())
+    announce(f"{n} pairs: {got} offending (oracle {want})")
+    assert got == want
+    if n >= 7:
+        assert want > 0
 
 
 def test_validate_tables_counts():
