@@ -88,6 +88,15 @@ def assert_pool_equal(got: np.ndarray, want: np.ndarray) -> None:
     assert not diff.any(), f"{int(diff.sum())} elements differ"
 
 
+def frob_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_F / ||ref||_F over the whole output (reported beside the
+    per-row figure)."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    den = float(np.linalg.norm(r))
+    return float(np.linalg.norm(g - r)) / (den if den > 0 else 1.0)
+
+
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     """max over (seq, head) rows of max_d |got - ref| / max_d |ref|."""
     g = got.reshape(-1, got.shape[-1]).astype(np.float64)
