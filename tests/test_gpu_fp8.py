@@ -130,6 +130,7 @@ CASES = {
     "gqa8-d64": _fp8(lambda: W.scaled("f8-g8", 122, 7, 1, 500, 16, 2, 64, "bf16")),
     "mha-d128-b8": _fp8(lambda: W.scaled("f8-m", 123, 5, 1, 300, 4, 4, 128, "bf16", block_size=8)),
     "gqa3-d64-b32": _fp8(lambda: W.scaled("f8-g3", 124, 4, 1, 400, 6, 2, 64, "bf16", block_size=32)),
+    "gqa16-d128": _fp8(lambda: W.scaled("f8-g16", 130, 5, 1, 500, 16, 1, 128, "bf16")),
     "cow": _fp8(lambda: W.shared_prefix("f8-cow", 125, "bf16", 2, 6, 67, 1, 40, 8, 2, 128, 200)),
     "saturating": lambda: W.Workload(**{**W.scaled("f8-sat", 126, 5, 1, 300, 8, 2, 128, "bf16").__dict__,
                                        "dtype": "fp8", "k_scales": [1.5 / 448, 2.5 / 448],
