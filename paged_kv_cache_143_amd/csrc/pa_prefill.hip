@@ -18,7 +18,8 @@
 // heads of the group.  A wavefront owns NQ column groups and walks the
 // sequence's keys from position 0 up to its last row's position: S^T = K q^T
 // on the matrix cores, a causal mask per column, online softmax, O^T += V^T
-// P^T with P split into high and low 16-bit halves.  Each K/V fragment serves
+// P^T with P split into high and low bf16 halves (bf16 pools) or rounded once
+// to fp16 (fp16 and FP8 pools).  Each K/V fragment serves
 // NQ groups; the four wavefronts of a workgroup take consecutive row ranges of
 // one (sequence, KV head).
 //
@@ -29,8 +30,8 @@
 // and every wavefront reads its fragments from LDS, the next step's K while
 // the current step's softmax runs.  Table entries come in
 // windows of 64 blocks, one per lane, and reach the loading lanes by lane
-// permutation; FP8 codes land raw and are widened to the 16-bit layout in LDS
-// once per workgroup.  fp32 pools (prefill_kernel): each wavefront walks on
+// permutation; FP8 codes land raw and are widened in LDS once per workgroup,
+// K to bf16 and V to fp16.  fp32 pools (prefill_kernel): each wavefront walks on
 // its own, one sub-tile per step with a second buffer one step ahead, through
 // cached buffer loads.  Each XCD runs the row tiles of one (sequence, KV head)
 // after another, last rows (the most keys) first, so its resident workgroups
@@ -47,7 +48,7 @@ namespace pa {
 // 32 keys per step: the P.V product's k dimension holds 4 tokens of each
 // sub-tile per lane group (k slots 0..3: sub-tile a, 4..7: sub-tile b), so
 // the V operand is two 8-byte loads side by side -- no duplicated V -- and
-// the high and low 16-bit parts of P are two products with the same V.  The
+// with bf16 V the high and low parts of P are two products with the same V.  The
 // masks for stored-length tails and causal limits run only on partial
 // steps; P is narrowed two values per conversion.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -58,6 +59,11 @@ template <> __device__ inline uint32_t pack2<TagBF16>(f32x2 x) {
 template <> __device__ inline uint32_t pack2<TagF16>(f32x2 x) {
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+}
+// Two E4M3 codes (bytes 2*hi, 2*hi+1 of w) -> two fp16 (exact: E4M3's 3
+// mantissa bits and exponents 2^-9 .. 2^8 lie inside fp16's).
+template <bool Hi> __device__ inline uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, Hi));
 }
 template <class Tag> __device__ inline f32x2 unpack2(uint32_t w);
 template <> __device__ inline f32x2 unpack2<TagBF16>(uint32_t w) {
@@ -148,13 +154,14 @@ __device__ inline void rebase(f32x4 sa, f32x4 sb, State<D>& st, float c, float* 
 // l += sum p; acc += V^T P^T.  bf16: P split into high and low 16-bit parts
 // (two products with the same V fragment; one bf16 rounding of P, 2^-9
 // relative, measures 2.4e-3 row error on N(0,1) data, above the 2e-3 bar).
-// fp16: one product with P rounded to fp16 (2^-11 relative, p <= 2^8 well
-// inside its range), which keeps the result within the bar on its own.  V
+// fp16 (fp16 pools, and FP8 pools whose V codes widen to fp16 exactly): one
+// product with P rounded to fp16 (2^-11 relative, p <= 2^8 well inside its
+// range), which keeps the result within the bar on its own.  V
 // rows of invalid keys must be zero (their p is 0, but 0 * NaN is NaN).
 template <class Tag> struct SplitP { static constexpr bool value = true; };
 template <> struct SplitP<TagF16> { static constexpr bool value = false; };
-template <class Tag, int D>
-__device__ inline void accumulate(const FragPair<Tag, D>& f, const float* p, State<D>& st) {
+template <class Tag, class FTag, int D>
+__device__ inline void accumulate(const FragPair<FTag, D>& f, const float* p, State<D>& st) {
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   u32x4 hi, lo;
 #pragma unroll
@@ -282,6 +289,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   using RG = Ring<Tag, D>;
   using CT = typename ComputeTag<Tag>::type;   // FP8 codes become bf16 in the slots
   constexpr bool F8 = RG::kF8;
+  using PT = std::conditional_t<F8, TagF16, CT>;   // P.V: FP8 V codes become fp16
   constexpr int ES = Elt<Tag>::bytes;
   __shared__ __attribute__((aligned(1024))) char ring[RG::kBytes];
   const int lane = threadIdx.x & (kWave - 1);
@@ -465,8 +473,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   // that publishes the stage).  16-bit pools: on a step with invalid keys the
   // V-loading lanes zero those keys' elements (a tail past L or a block
   // outside the pool may hold NaN, and 0 * NaN would reach the accumulators).
-  // FP8 pools: every lane widens its raw codes to the bf16 fragments of the
-  // stage's 16-bit slot (exact: every E4M3 value is a bf16 value), V with the
+  // FP8 pools: every lane widens its raw codes into the stage's 16-bit slot,
+  // K to bf16 and V to fp16 (both exact for every E4M3 value), V with the
   // same zeroing.  V piece of lane (d, tg) holds tokens 4 tg .. 4 tg + 3.
   auto v_keep = [&](uint32_t valid, int tile, uint32_t& k0, uint32_t& k1) {
     const uint32_t bits = valid >> (16 * tile + 4 * (F8 ? lane >> 4 : (lane >> 3) & 3));
@@ -497,7 +505,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             *reinterpret_cast<u32x2*>(slot + RG::kKBytes + (4 * pc + e) * 1024 + h * 512 + lane * 8) =
-                u32x2{fp8x2_to_bf16x2<false>(x[e]) & k0, fp8x2_to_bf16x2<true>(x[e]) & k1};
+                u32x2{fp8x2_to_f16x2<false>(x[e]) & k0, fp8x2_to_f16x2<true>(x[e]) & k1};
         }
       }
       lgkm_wait<0>();
@@ -564,7 +572,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
       for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
     }
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) accumulate<CT, D>(f, p[q], st[q]);
+    for (int q = 0; q < NQ; ++q) accumulate<PT>(f, p[q], st[q]);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       sa[q] = na[q];

@@ -146,7 +146,10 @@ def _sampled(w, picks):
 @pytest.mark.parametrize("make,picks", [
     (W.prefill_bf16, [(0, 0), (0, 2047), (3, 1000), (7, 15), (15, 2046), (15, 511)]),
     (W.chunked_prefill_bf16, [(0, 0), (0, 511), (9, 255), (20, 100), (31, 511)]),
-], ids=["prefill-bf16-16x2048", "chunked-prefill-bf16-32x512"])
+    (W.prefill_fp8, [(0, 0), (0, 2047), (5, 1777), (15, 2047), (11, 33)]),
+    (W.prefill_opt13b_f16, [(0, 0), (0, 2047), (4, 1500), (7, 2046)]),
+], ids=["prefill-bf16-16x2048", "chunked-prefill-bf16-32x512", "prefill-fp8-16x2048",
+        "prefill-opt13b-f16-8x2048"])
 def test_full_size_sampled(make, picks):
     w = make()
     got, _, _ = _run(w)
