@@ -9,7 +9,10 @@ on their own:
   at a per-lane offset inside one block's tile of the KV head, and read back
   by fragment loads at fixed LDS offsets (FP8 pools: raw codes, widened to
   bf16 fragments by the lanes that loaded them);
-* the paired 8-token decode tiles (pa_decode.hip, load_pair8).
+* the paired 8-token decode tiles (pa_decode.hip, load_pair8);
+* the 16-row decode tiles of 16-bit pools with 16- and 32-token blocks
+  (pa_decode.hip, load_tile16), whose out-of-pool and past-the-end tiles
+  address block 0 of the pool.
 
 This test re-derives those lane offsets, written as in the kernels, for every
 supported block size and head dim, and checks them against the tile sizes of
@@ -145,6 +148,39 @@ def test_decode_pair8_loads_in_bounds(D):
     for pieces, w in ((k, 16), (v, 8)):
         for blk in (0, 1):
             assert len({o + i for b, o in pieces if b == blk for i in range(w)}) == block_bytes
+
+
+def decode_tile16_offsets(D):
+    """(byte offset, width) of every lane's K and V pieces in one 16-row
+    sub-tile, as load_tile16 forms them (K and V offsets relative to the
+    sub-tile's K and V starts)."""
+    k, v = [], []
+    for lane in range(64):
+        for m in range(D // 32):
+            k.append((lane & 15) * 64 + (lane >> 4) * 16 + m * 16 * 64)
+        for n in range(D // 16):
+            v.append((lane >> 4) * (D * 8) + (lane & 15) * 8 + n * 128)
+    return k, v
+
+
+@pytest.mark.parametrize("b", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_tile16_loads_in_bounds(b, D):
+    """Each piece lies inside its 16-row sub-tile, the pieces cover the
+    sub-tile's bytes exactly once, and every sub-tile of the block (the
+    sub-tile offset of open_table, (j mod b/16) * sub-tile bytes) lies inside
+    the block's tile of the KV head -- so any block in the pool, block 0
+    included, is a safe address."""
+    sub_bytes = 16 * D * 2
+    tile_bytes = b * D * 2
+    k, v = decode_tile16_offsets(D)
+    for pieces, w in ((k, 16), (v, 8)):
+        for o in pieces:
+            assert 0 <= o and o + w <= sub_bytes
+        covered = [o + i for o in pieces for i in range(w)]
+        assert len(covered) == len(set(covered)) == sub_bytes
+    for j in range(b // 16):
+        assert 0 <= j * sub_bytes and (j + 1) * sub_bytes <= tile_bytes
 
 
 def ring_dma_fp8(b, D):
