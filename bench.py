@@ -62,6 +62,13 @@ def _workloads():
                               "uniform int 200..2000, 8-token blocks"),
         "gqa-bf16-b256-bs32": (lambda: W.gqa_bf16_block(32), 0,
                                "uniform int 200..2000, 32-token blocks"),
+        # one GPU's share under 8-way head sharding (tensor parallel by KV head)
+        "gqa-bf16-b256-tp8": (W.gqa_bf16_tp8, -1, "uniform int 200..2000, 4 q / 1 kv heads"),
+        "long-ctx-splitk-bf16-tp8": (W.long_ctx_bf16_tp8, -1,
+                                     "uniform int 8192..32768, 8 q / 1 kv heads"),
+        "opt13b-mha-f16-tp8": (W.opt13b_f16_tp8, -1, "uniform int 200..2000, 5 / 5 heads"),
+        # one GPU's share under 8-way sequence sharding
+        "gqa-bf16-b256-dp8": (W.gqa_bf16_dp8, -1, "every 8th sequence of gqa-bf16-b256 (32)"),
         "tiny-f32": (W.tiny_f32, 0, "{50, 20, 65, 16}"),
         "swap-gqa-bf16": (W.swap_gqa_bf16, 0,
                           "uniform int 200..2000; every third sequence swapped out and back"),

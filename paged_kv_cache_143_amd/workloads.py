@@ -474,3 +474,43 @@ def gqa_bf16_block(block_size: int, num_seqs: int = 256, seed: int = 3) -> Workl
     lengths = _uniform_lengths(rng, num_seqs, 200, 2000)
     return independent(f"gqa-bf16-b256-bs{block_size}", seed, "bf16", lengths, 32, 8, 128,
                        _pool_for(lengths, block_size, 0.0), block_size=block_size)
+
+
+def head_shard(w: Workload, ways: int, name: str) -> Workload:
+    """One GPU's share of `w` when its KV heads are split `ways` ways (tensor
+    parallel by head): the same sequences, lengths, block size and pool, with
+    Hq / ways query heads on Hkv / ways KV heads.  Payload values are drawn
+    for the shard's own shape (seeded like the whole workload)."""
+    if w.num_kv_heads % ways:
+        raise ValueError(f"{w.num_kv_heads} KV heads do not split {ways} ways")
+    return Workload(name=name, seed=w.seed, dtype=w.dtype, num_blocks=w.num_blocks,
+                    block_size=w.block_size, num_q_heads=w.num_q_heads // ways,
+                    num_kv_heads=w.num_kv_heads // ways, head_dim=w.head_dim, ops=w.ops,
+                    free_order=w.free_order, seq_names=w.seq_names, data_len=w.data_len,
+                    partition_size=-1, notes=f"{ways}-way head shard of {w.name}")
+
+
+def gqa_bf16_tp8() -> Workload:
+    """Batch-256 GQA step as one of 8 GPUs sees it under head sharding: 4 q / 1 kv heads."""
+    return head_shard(gqa_bf16(), 8, "gqa-bf16-b256-tp8")
+
+
+def long_ctx_bf16_tp8() -> Workload:
+    """Long-context batch as one of 8 GPUs sees it under head sharding: 8 q / 1 kv heads."""
+    return head_shard(long_ctx_bf16(), 8, "long-ctx-splitk-bf16-tp8")
+
+
+def opt13b_f16_tp8() -> Workload:
+    """OPT-13B-shaped layer as one of 8 GPUs sees it under head sharding: 5 / 5 heads."""
+    return head_shard(opt13b_f16(), 8, "opt13b-mha-f16-tp8")
+
+
+def gqa_bf16_dp8() -> Workload:
+    """Batch-256 GQA step as one of 8 GPUs sees it under sequence sharding:
+    every eighth sequence of the batch (32, the same lengths), all 32 / 8 heads."""
+    rng = np.random.default_rng(3 + 100)
+    lengths = _uniform_lengths(rng, 256, 200, 2000)[::8]
+    w = independent("gqa-bf16-b256-dp8", 3, "bf16", lengths, 32, 8, 128,
+                    _pool_for(lengths, 16, 0.0))
+    w.partition_size = -1
+    return w

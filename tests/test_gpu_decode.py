@@ -403,6 +403,12 @@ FULL = {
     "gqa-in-order": (W.gqa_bf16_in_order, 0, None),
     "long-ctx-splitk": (W.long_ctx_bf16, 512, None),
     "long-ctx-auto": (W.long_ctx_bf16, -1, None),
+    # one GPU's share under 8-way head sharding
+    "gqa-b256-tp8": (W.gqa_bf16_tp8, -1, None),
+    "long-ctx-tp8": (W.long_ctx_bf16_tp8, -1, None),
+    "opt13b-tp8": (W.opt13b_f16_tp8, -1, None),
+    # one GPU's share under 8-way sequence sharding
+    "gqa-b256-dp8": (W.gqa_bf16_dp8, -1, None),
 }
 
 
