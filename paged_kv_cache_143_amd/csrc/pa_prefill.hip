@@ -160,21 +160,32 @@ __device__ inline void rebase(f32x4 sa, f32x4 sb, State<D>& st, float c, float* 
 // rows of invalid keys must be zero (their p is 0, but 0 * NaN is NaN).
 template <class Tag> struct SplitP { static constexpr bool value = true; };
 template <> struct SplitP<TagF16> { static constexpr bool value = false; };
-template <class Tag, class FTag, int D>
-__device__ inline void accumulate(const FragPair<FTag, D>& f, const float* p, State<D>& st) {
-  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+
+// The two halves of a step's P.V: narrow_p (l += sum p, P narrowed to the
+// product's 16-bit type) runs while the step's LDS reads are in flight,
+// pv_products (acc += V^T P^T) after them.
+struct PPack {
   u32x4 hi, lo;
+};
+template <class Tag, int D>
+__device__ inline PPack narrow_p(const float* p, State<D>& st) {
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  PPack pk;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const f32x2 pw = {p[2 * w], p[2 * w + 1]};
-    hi[w] = pack2<Tag>(pw);
-    if constexpr (SplitP<Tag>::value) lo[w] = pack2<Tag>(pw - unpack2<Tag>(hi[w]));
+    pk.hi[w] = pack2<Tag>(pw);
+    if constexpr (SplitP<Tag>::value) pk.lo[w] = pack2<Tag>(pw - unpack2<Tag>(pk.hi[w]));
   }
+  return pk;
+}
+template <class Tag, class FTag, int D>
+__device__ inline void pv_products(const FragPair<FTag, D>& f, const PPack& pk, State<D>& st) {
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(f.v[n], hi, st.acc[n]);
+  for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(f.v[n], pk.hi, st.acc[n]);
   if constexpr (SplitP<Tag>::value) {
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(f.v[n], lo, st.acc[n]);
+    for (int n = 0; n < D / 16; ++n) st.acc[n] = mma32<Tag>(f.v[n], pk.lo, st.acc[n]);
   }
 }
 
@@ -528,10 +539,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
 
   // Step j (stage S = j % 4), software-pipelined across steps: the scores
   // S^T of step j were computed during step j - 1.  Read V of step j and K of
-  // step j + 1 from LDS; mask step j's scores where needed; take the
-  // exponentials of step j while the matrix cores compute step j + 1's
-  // scores; then P.V of step j, whose products overlap the narrowing of P.
-  // LDS reads complete in order.  On the last step the next stage holds no
+  // step j + 1 from LDS; while those reads are in flight, mask step j's
+  // scores where needed, take its exponentials (and move the base if one
+  // exceeds 2^8) and narrow P; then, held behind a scheduling barrier so that
+  // the compiler does not sink that vector work into the matrix phase, step
+  // j + 1's scores and step j's P.V products (measured: 820 -> 795 us on 16 x
+  // 2048 prompts).  LDS reads complete in order.  On the last step the next stage holds no
   // step (stale or never written LDS): its scores are computed and unused,
   // which keeps the step free of branches.
   const uint32_t ka = lds0 + lane * 16, va = lds0 + lane * 8;
@@ -558,6 +571,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     bool fix = false;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) fix |= take_exps<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
+    if (__builtin_amdgcn_ballot_w64(fix) != 0) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
+    }
+    PPack pk[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) pk[q] = narrow_p<PT, D>(p[q], st[q]);
+    // The softmax of this step runs while its LDS reads are in flight; the
+    // matrix products wait for them.
+    __builtin_amdgcn_sched_barrier(0);
     lgkm_wait<0>();                     // V of this step and K of the next
 #pragma unroll
     for (int d = 0; d < D / 16; ++d) reg_after(f.v[d]);
@@ -567,12 +590,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
 #pragma unroll
       for (int m = 0; m < RG::kChunks; ++m) reg_after(f.k[h][m]);
     scores(na, nb);
-    if (__builtin_amdgcn_ballot_w64(fix) != 0) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) accumulate<PT>(f, p[q], st[q]);
+    for (int q = 0; q < NQ; ++q) pv_products<PT>(f, pk[q], st[q]);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       sa[q] = na[q];
