@@ -453,7 +453,7 @@ def run_prefill(args, w, length_desc):
                        "attention_p90": round(float(np.percentile(att_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "mfma", "achieved": round(att_tf, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(att_tf / peak, 4), "traffic": None,
-                     "kernel": "pa_prefill_attention (" + ("prefill_ring_kernel" if w.dtype in ("bf16", "f16")
+                     "kernel": "pa_prefill_attention (" + ("prefill_ring_kernel" if w.dtype in ("bf16", "f16", "fp8")
                                                          else "prefill_kernel") + ")",
                      "algorithmic_flops": flops},
     }
