@@ -116,28 +116,26 @@ __device__ inline void mask_scores(f32x4& sa, f32x4& sb, uint32_t valid, float c
 }
 
 // p = exp2(c s - base) against the column's current base (0 while it has
-// none); returns whether the column needs the exact path: some p > 2^8
-// (= 256.0f; p >= 0, so an integer maximum of the bit patterns finds it) or
+// none) and their sum; returns whether the column needs the exact path: the
+// sum exceeds 2^8 (every p > 2^8 is caught, since p >= 0; now and then a
+// step whose p are all below that moves the base too, which is harmless) or
 // no base yet.
 template <int D>
-__device__ inline bool take_exps(f32x4 sa, f32x4 sb, const State<D>& st, float c, float* p) {
+__device__ inline bool take_exps(f32x4 sa, f32x4 sb, const State<D>& st, float c, float* p, float& sum) {
   const float base = st.m == -INFINITY ? 0.f : st.m;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     p[r] = fast_exp2(__builtin_fmaf(sa[r], c, -base));
     p[4 + r] = fast_exp2(__builtin_fmaf(sb[r], c, -base));
   }
-  const uint32_t pm = max(max(max(__float_as_uint(p[0]), __float_as_uint(p[1])),
-                              max(__float_as_uint(p[2]), __float_as_uint(p[3]))),
-                          max(max(__float_as_uint(p[4]), __float_as_uint(p[5])),
-                              max(__float_as_uint(p[6]), __float_as_uint(p[7]))));
-  return pm > 0x43800000u || st.m == -INFINITY;
+  sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  return !(sum <= 256.f) || st.m == -INFINITY;
 }
 
 // The exact path (rare): move the base to the running maximum, rescale l and
 // acc, and take the exponentials again -- the same softmax for any base.
 template <int D>
-__device__ inline void rebase(f32x4 sa, f32x4 sb, State<D>& st, float c, float* p) {
+__device__ inline void rebase(f32x4 sa, f32x4 sb, State<D>& st, float c, float* p, float& sum) {
   float bm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) bm = fmaxf(bm, fmaxf(sa[r] * c, sb[r] * c));
@@ -148,7 +146,7 @@ __device__ inline void rebase(f32x4 sa, f32x4 sb, State<D>& st, float c, float* 
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) st.acc[n] *= alpha;
   st.m = m_new;
-  take_exps<D>(sa, sb, st, c, p);
+  take_exps<D>(sa, sb, st, c, p, sum);
 }
 
 // l += sum p; acc += V^T P^T.  bf16: P split into high and low 16-bit parts
@@ -167,15 +165,25 @@ template <> struct SplitP<TagF16> { static constexpr bool value = false; };
 struct PPack {
   u32x4 hi, lo;
 };
+// The low part of bf16 P, p - hi (exact), one packed bf16 dot product per
+// value: hi . (-1, 0) + p0 and hi . (0, -1) + p1.  The pairs come in scalar
+// registers (neg.x = 0x0000bf80, neg.y = 0xbf800000): as an immediate the
+// compiler encodes (-1, 0) as the inline constant -1.0, which the hardware
+// does not read as that pair.
+__device__ inline f32x2 minus_hi(uint32_t hi, f32x2 p, uint2 neg) {
+  const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
+  return f32x2{__builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg.x), p[0], false),
+               __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, neg.y), p[1], false)};
+}
 template <class Tag, int D>
-__device__ inline PPack narrow_p(const float* p, State<D>& st) {
-  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+__device__ inline PPack narrow_p(const float* p, float sum, State<D>& st, uint2 neg) {
+  st.l += sum;
   PPack pk;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const f32x2 pw = {p[2 * w], p[2 * w + 1]};
     pk.hi[w] = pack2<Tag>(pw);
-    if constexpr (SplitP<Tag>::value) pk.lo[w] = pack2<Tag>(pw - unpack2<Tag>(pk.hi[w]));
+    if constexpr (SplitP<Tag>::value) pk.lo[w] = pack2<Tag>(minus_hi(pk.hi[w], pw, neg));
   }
   return pk;
 }
@@ -548,6 +556,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   // step (stale or never written LDS): its scores are computed and unused,
   // which keeps the step free of branches.
   const uint32_t ka = lds0 + lane * 16, va = lds0 + lane * 8;
+  uint2 neg = {0x0000bf80u, 0xbf800000u};   // bf16 pairs (-1, 0), (0, -1): minus_hi
+  asm("" : "+s"(neg.x));
+  asm("" : "+s"(neg.y));
   FragPair<CT, D> f;                    // f.k: next step's K, f.v: this step's V
   f32x4 sa[NQ], sb[NQ];                 // this step's scores
   auto scores = [&](f32x4* xa, f32x4* xb) {
@@ -567,17 +578,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
 #pragma unroll
       for (int q = 0; q < NQ; ++q) mask_scores<D>(sa[q], sb[q], valid, qk_scale, lane, pos[q] - key0 + 1);
     }
-    float p[NQ][8];
+    float p[NQ][8], ps[NQ];
     bool fix = false;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) fix |= take_exps<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
+    for (int q = 0; q < NQ; ++q) fix |= take_exps<D>(sa[q], sb[q], st[q], qk_scale, p[q], ps[q]);
     if (__builtin_amdgcn_ballot_w64(fix) != 0) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], qk_scale, p[q]);
+      for (int q = 0; q < NQ; ++q) rebase<D>(sa[q], sb[q], st[q], qk_scale, p[q], ps[q]);
     }
     PPack pk[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) pk[q] = narrow_p<PT, D>(p[q], st[q]);
+    for (int q = 0; q < NQ; ++q) pk[q] = narrow_p<PT, D>(p[q], ps[q], st[q], neg);
     // The softmax of this step runs while its LDS reads are in flight; the
     // matrix products wait for them.
     __builtin_amdgcn_sched_barrier(0);

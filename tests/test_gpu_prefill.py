@@ -77,6 +77,9 @@ CASES = {
 }
 
 
+SPLIT_ROW_BOUND = 3e-5
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_prefill_matches_oracle(name):
     w = CASES[name]()
@@ -87,6 +90,10 @@ def test_prefill_matches_oracle(name):
     err = row_rel_err(got, ref)
     announce(f"{name}: max row rel err {err:.3e}")
     assert err <= tol_for(w.dtype)
+    if w.dtype == "bf16":
+        # P in two bf16 halves keeps fp32-level rows (measured <= 1e-5); a
+        # single rounding of P, or a wrong low half, lands near 1e-3.
+        assert err <= SPLIT_ROW_BOUND
 
 
 # Row bound of a 16-bit prefill output against the oracle, besides one ulp of
