@@ -261,7 +261,10 @@ template <class Tag, int D> struct Ring {
   static constexpr int kRawChunks = D / 64;               // FP8 pieces per tile, K or V
   static constexpr int kRawStep = kStep / 2;
   static constexpr int kStages = kF8 ? 3 : PA_RING_STAGES;
-  static constexpr int kAhead = kStages - 1;               // steps loaded ahead
+  // Steps loaded ahead.  FP8: 4, and a step's codes are widened into their
+  // slot two steps before its scores (during the softmax of step j - 2),
+  // three raw stages (j + 2 .. j + 4) and three slots (j .. j + 2).
+  static constexpr int kAhead = kF8 ? 4 : kStages - 1;
   static constexpr int kRawBase = kStages * kStep;          // FP8 raw stages after the slots
   static constexpr int kBytes = kStages * kStep + (kF8 ? kStages * kRawStep : 0);
   static constexpr int kPerWave = (kF8 ? kRawStep : kStep) / 1024 / kPWaves;  // loads per step
@@ -296,6 +299,10 @@ __device__ inline void reg_after(u32x4& x) { asm volatile("" : "+v"(x)); }
 template <int Base, class Tag, int D, int... I>
 __device__ inline void read_k(FragPair<Tag, D>& f, uint32_t ka, std::integer_sequence<int, I...>) {
   ((f.k[I / (D / 32)][I % (D / 32)] = lds_read_b128<Base + I * 1024>(ka)), ...);
+}
+template <int Base, int... I>
+__device__ inline void read_raw(u32x4* x, uint32_t addr, std::integer_sequence<int, I...>) {
+  ((x[I] = lds_read_b128<Base + I * 1024>(addr)), ...);
 }
 template <int Base, class Tag, int D, int... I>
 __device__ inline void read_v(FragPair<Tag, D>& f, uint32_t va, std::integer_sequence<int, I...>) {
@@ -500,33 +507,40 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     k0 = (bits & 1u ? 0x0000ffffu : 0u) | (bits & 2u ? 0xffff0000u : 0u);
     k1 = (bits & 4u ? 0x0000ffffu : 0u) | (bits & 8u ? 0xffff0000u : 0u);
   };
+  // FP8: widen this lane's raw pieces x (of the step in raw stage rs) into
+  // slot stg.  land() reads the pieces itself; the main loop reads them
+  // early (raw_read) and widens them during the softmax.
+  auto widen = [&](int stg, uint32_t valid, const u32x4* x) {
+    char* slot = ring + stg * RG::kStep;
+    if (wave < 2) {                     // K of tile `wave`: piece p -> fragments m = 2p, 2p + 1
+#pragma unroll
+      for (int pc = 0; pc < RG::kRawChunks; ++pc)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          *reinterpret_cast<u32x4*>(slot + (wave * RG::kChunks + 2 * pc + u) * 1024 + lane * 16) =
+              u32x4{fp8x2_to_bf16x2<false>(x[pc][2 * u]), fp8x2_to_bf16x2<true>(x[pc][2 * u]),
+                    fp8x2_to_bf16x2<false>(x[pc][2 * u + 1]), fp8x2_to_bf16x2<true>(x[pc][2 * u + 1])};
+    } else {                            // V of tile h: dword e of piece p is dim tile 4p + e
+      const int h = wave - 2;
+      uint32_t k0 = 0xffffffffu, k1 = 0xffffffffu;
+      if (valid != 0xffffffffu) v_keep(valid, h, k0, k1);
+#pragma unroll
+      for (int pc = 0; pc < RG::kRawChunks; ++pc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<u32x2*>(slot + RG::kKBytes + (4 * pc + e) * 1024 + h * 512 + lane * 8) =
+              u32x2{fp8x2_to_f16x2<false>(x[pc][e]) & k0, fp8x2_to_f16x2<true>(x[pc][e]) & k1};
+    }
+  };
+  const uint32_t rawa = lds0 + (uint32_t)(RG::kRawBase + wave * RG::kRawChunks * 1024 + lane * 16);
   auto land = [&](int stg, uint32_t valid) {
     if constexpr (F8) {
       const char* raw = ring + RG::kRawBase + stg * RG::kRawStep;
-      char* slot = ring + stg * RG::kStep;
-      if (wave < 2) {                   // K of tile `wave`: piece p -> fragments m = 2p, 2p + 1
+      u32x4 x[RG::kRawChunks];
 #pragma unroll
-        for (int pc = 0; pc < RG::kRawChunks; ++pc) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(raw + (wave * RG::kRawChunks + pc) * 1024 + lane * 16);
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            *reinterpret_cast<u32x4*>(slot + (wave * RG::kChunks + 2 * pc + u) * 1024 + lane * 16) =
-                u32x4{fp8x2_to_bf16x2<false>(x[2 * u]), fp8x2_to_bf16x2<true>(x[2 * u]),
-                      fp8x2_to_bf16x2<false>(x[2 * u + 1]), fp8x2_to_bf16x2<true>(x[2 * u + 1])};
-        }
-      } else {                          // V of tile h: dword e of piece p is dim tile 4p + e
-        const int h = wave - 2;
-        uint32_t k0 = 0xffffffffu, k1 = 0xffffffffu;
-        if (valid != 0xffffffffu) v_keep(valid, h, k0, k1);
-#pragma unroll
-        for (int pc = 0; pc < RG::kRawChunks; ++pc) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(raw + (wave * RG::kRawChunks + pc) * 1024 + lane * 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<u32x2*>(slot + RG::kKBytes + (4 * pc + e) * 1024 + h * 512 + lane * 8) =
-                u32x2{fp8x2_to_f16x2<false>(x[e]) & k0, fp8x2_to_f16x2<true>(x[e]) & k1};
-        }
-      }
+      for (int pc = 0; pc < RG::kRawChunks; ++pc)
+        x[pc] = *reinterpret_cast<const u32x4*>(raw + (wave * RG::kRawChunks + pc) * 1024 + lane * 16);
+      widen(stg, valid, x);
       lgkm_wait<0>();
     } else {
       if (wave >= 2 && valid != 0xffffffffu) {
@@ -565,18 +579,40 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
 #pragma unroll
     for (int q = 0; q < NQ; ++q) qk_pair<CT, D>(f, qf[q], xa[q], xb[q]);
   };
-  auto compute = [&](auto stage_c, int j, uint32_t valid) {
+  // vm_steps(k): wait until at most k steps' loads of this wavefront are
+  // outstanding.
+  auto vm_steps = [](int k) {
+    if (k >= 2) vm_wait<2 * RG::kPerWave>(); else if (k == 1) vm_wait<RG::kPerWave>(); else vm_wait<0>();
+  };
+  static_assert(F8 || RG::kAhead <= 3, "vm_steps covers up to two newer steps");
+  // Valid-key bits per slot (of the step whose K/V it holds); FP8 also per
+  // raw stage (of the step loading into it).
+  uint32_t valid[RG::kStages], vraw[RG::kStages];
+#pragma unroll
+  for (int i = 0; i < RG::kStages; ++i) valid[i] = vraw[i] = 0u;
+  auto compute = [&](auto stage_c, int j, uint32_t valid_j) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int S1 = (S + 1) % RG::kStages;
+    constexpr int S2 = (S + 2) % RG::kStages;
+    // FP8: the raw pieces of step j + 2, read between this step's V and K
+    // fragments and widened into their slot during the softmax.
+    u32x4 rx[RG::kRawChunks];
+    const bool widen_next = F8 && j + 2 < nsteps;
     read_v<S * RG::kStep + RG::kKBytes>(f, va, std::make_integer_sequence<int, D / 16>());
+    if constexpr (F8) {
+      if (widen_next) {
+        vm_steps(nsteps - 3 - j);         // this lane's loads of step j + 2 have landed
+        read_raw<S2 * RG::kRawStep>(rx, rawa, std::make_integer_sequence<int, RG::kRawChunks>());
+      }
+    }
     read_k<S1 * RG::kStep>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
     const int key0 = 32 * j;
-    bool need = valid != 0xffffffffu;
+    bool need = valid_j != 0xffffffffu;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) need |= __builtin_amdgcn_ballot_w64(pos[q] - key0 + 1 < 2 * kRows) != 0;
     if (need) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) mask_scores<D>(sa[q], sb[q], valid, qk_scale, lane, pos[q] - key0 + 1);
+      for (int q = 0; q < NQ; ++q) mask_scores<D>(sa[q], sb[q], valid_j, qk_scale, lane, pos[q] - key0 + 1);
     }
     float p[NQ][8], ps[NQ];
     bool fix = false;
@@ -589,6 +625,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     PPack pk[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) pk[q] = narrow_p<PT, D>(p[q], ps[q], st[q], neg);
+    if constexpr (F8) {
+      if (widen_next) {
+        lgkm_wait<2 * RG::kChunks>();     // V fragments and the raw pieces (K may be in flight)
+#pragma unroll
+        for (int pc = 0; pc < RG::kRawChunks; ++pc) reg_after(rx[pc]);
+        widen(S2, vraw[S2], rx);
+        valid[S2] = vraw[S2];
+      }
+    }
     // The softmax of this step runs while its LDS reads are in flight; the
     // matrix products wait for them.
     __builtin_amdgcn_sched_barrier(0);
@@ -617,21 +662,34 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
   // still run), so after it every wavefront may read step j + 1's K.
   // vm_steps(k): wait until at most k steps' loads of this wavefront are
   // outstanding.
-  auto vm_steps = [](int k) {
-    if (k >= 2) vm_wait<2 * RG::kPerWave>(); else if (k == 1) vm_wait<RG::kPerWave>(); else vm_wait<0>();
-  };
-  static_assert(RG::kAhead <= 3, "vm_steps covers up to two newer steps");
-  uint32_t valid[RG::kStages];
-#pragma unroll
-  for (int i = 0; i < RG::kStages; ++i) valid[i] = 0u;
-  for (int i = 0; i < RG::kAhead && i < nsteps; ++i) {
+  auto start = [&](int i) {             // loads of step i into stage i % kStages
     const Prep pr = prepare(i);
-    valid[i] = pr.valid;
-    dma(pr, i);
+    (F8 ? vraw : valid)[i % RG::kStages] = pr.valid;
+    dma(pr, i % RG::kStages);
+  };
+  if constexpr (F8) {
+    // Steps 0 and 1 are widened before the first barrier; step 3's loads
+    // reuse step 0's raw stage once this lane has widened it.
+    for (int i = 0; i < 3 && i < nsteps; ++i) start(i);
+    if (nsteps > 0) {
+      vm_steps(min(2, nsteps - 1));
+      valid[0] = vraw[0];
+      land(0, valid[0]);
+      if (nsteps > 3) start(3);
+    }
+    if (nsteps > 1) {
+      vm_steps((nsteps > 2) + (nsteps > 3));
+      valid[1] = vraw[1];
+      land(1, valid[1]);
+    }
+  } else {
+    for (int i = 0; i < RG::kAhead && i < nsteps; ++i) start(i);
+    if (nsteps > 0) {
+      vm_steps(min(RG::kAhead, nsteps) - 1);
+      land(0, valid[0]);
+    }
   }
   if (nsteps > 0) {
-    vm_steps(min(RG::kAhead, nsteps) - 1);
-    land(0, valid[0]);
     __builtin_amdgcn_s_barrier();
     read_k<0>(f, ka, std::make_integer_sequence<int, 2 * RG::kChunks>());
     lgkm_wait<0>();
@@ -648,13 +706,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_ring_kernel(PrefillArgs a) 
     Prep pr;
     const bool more = j + RG::kAhead < nsteps;
     if (more) pr = prepare(j + RG::kAhead);
-    if (j + 1 < nsteps) {
-      vm_steps(min(RG::kAhead - 2, nsteps - j - 2));
-      land(S1, valid[S1]);                // this wavefront's loads of step j + 1 are done
+    if constexpr (!F8) {
+      if (j + 1 < nsteps) {
+        vm_steps(min(RG::kAhead - 2, nsteps - j - 2));
+        land(S1, valid[S1]);              // this wavefront's loads of step j + 1 are done
+      }
     }
     __builtin_amdgcn_s_barrier();
     if (more) {
-      valid[SA] = pr.valid;
+      (F8 ? vraw : valid)[SA] = pr.valid;
       dma(pr, SA);
     }
     compute(stage_c, j, valid[S]);
